@@ -1,0 +1,51 @@
+"""The oracle pins must fail when a plausible mistake is planted in the oracle.
+
+Each case copies ``oracle/``, ``synthetic/`` and the pin tests into a temporary
+directory, edits one line of the copied oracle, and runs the pins there in a
+subprocess.  The repository's own oracle is never modified.  CPU only.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTATIONS = {
+    "tail_keeps_H_plus_1": ("self.banks[k] = bank[-cfg.history:]", "self.banks[k] = bank[-(cfg.history + 1):]"),
+    "tail_keeps_oldest": ("self.banks[k] = bank[-cfg.history:]", "self.banks[k] = bank[:cfg.history]"),
+    "scale_one_over_d": ("return 1.0 / math.sqrt(self.head_dim)", "return 1.0 / self.head_dim"),
+    "lse_without_max": ("LSE[h] = m + np.log(l)", "LSE[h] = np.log(l)"),
+    "own_chunk_dropped": ('+ [("own", i)]', ""),
+    "gamma_right_anchor_floor": ("hi = -(-pos[-1] // D) * D", "hi = (pos[-1] // D) * D"),
+    "wrong_head_of_K": ("s = scale * (Q[:, h, :] @ K[:, h, :].T)", "s = scale * (Q[:, h, :] @ K[:, (h + 1) % nh, :].T)"),
+    "history_reversed": ("hist = [cid for cid, _, _ in self.banks[k]]",
+                         "hist = [cid for cid, _, _ in self.banks[k]][::-1]"),
+    "no_stage_dependency": ("if k > 0 and self.next_chunk[k - 1] <= i:", "if False:"),
+    "cap_drops_newest": ("hist = hist[1:]", "hist = hist[:-1]"),
+    "anchor_grid_shifted": ("return list(range(0, cfg.n_latents, cfg.anchor_stride))",
+                            "return list(range(cfg.anchor_stride, cfg.n_latents, cfg.anchor_stride))"),
+    "softmax_sign": ("p = np.exp(s - m[:, None])", "p = np.exp(m[:, None] - s)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTATIONS[name]
+    for d in ("oracle", "synthetic"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("__pycache__"))
+    (tmp_path / "tests").mkdir()
+    shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "tests" / "golden")
+    for f in ("conftest.py", "test_oracle_pins.py"):
+        shutil.copy(os.path.join(ROOT, "tests", f), tmp_path / "tests" / f)
+    src_path = tmp_path / "oracle" / "flashforward.py"
+    src = src_path.read_text()
+    assert old in src, f"mutation {name} no longer applies"
+    src_path.write_text(src.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        str(tmp_path / "tests" / "test_oracle_pins.py")],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"pins did not catch mutation {name}:\n{r.stdout[-2000:]}"
