@@ -1,0 +1,58 @@
+"""Build the native libraries in-tree.
+
+  libff.so            C ABI + gfx950 HIP kernels (hipcc, --offload-arch=gfx950)
+  libff_hostcheck.so  the same host bookkeeping linked against a recording stub
+                      instead of the kernels (g++); CPU tests use it to drive the
+                      ABI's success paths without a GPU.
+
+Run ``python -m chunked_kv_cache_amd.build`` (``__graft_entry__.build()`` calls it).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libff.so")
+HOSTCHECK = os.path.join(PKG, "libff_hostcheck.so")
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+# Packed fp32 VALU forms are kept out of every HIP object.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd):
+    print("+", " ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose_resources: bool = False) -> None:
+    os.makedirs(BUILD, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    host_src = os.path.join(CSRC, "host", "ff_host.cpp")
+    host_obj = os.path.join(BUILD, "ff_host.o")
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c", host_src, "-o", host_obj])
+
+    kern_src = os.path.join(CSRC, "hip", "ff_kernels.hip")
+    kern_obj = os.path.join(BUILD, "ff_kernels.o")
+    extra = ["-Rpass-analysis=kernel-resource-usage"] if verbose_resources else []
+    _run([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS, *extra, *inc,
+          "-c", kern_src, "-o", kern_obj])
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", host_obj, kern_obj, "-o", tmp])
+    os.replace(tmp, LIB)
+
+    stub_src = os.path.join(CSRC, "host", "device_stub.cpp")
+    tmp = HOSTCHECK + ".tmp"
+    _run(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall", *inc, host_src, stub_src, "-o", tmp])
+    os.replace(tmp, HOSTCHECK)
+
+
+if __name__ == "__main__":
+    build(verbose_resources="-v" in sys.argv)

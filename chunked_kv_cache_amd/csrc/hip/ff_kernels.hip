@@ -1,0 +1,609 @@
+// gfx950 kernels of the renderer hot path.
+//
+//  attn_bf16<D>   segmented flash attention: bf16 MFMA 32x32x16 for S^T = K Q^T
+//                 and O^T = V^T P^T, fp32 online softmax in base 2, K/V tiles
+//                 gathered from the anchor bank and the stage ring through the
+//                 call's key-source table into LDS (no concatenation copy).
+//  attn_f32<D>    plain fp32 path (one lane per query row and head).
+//  merge_splits   LSE merge of key-range splits.
+//  publish        token-major K/V -> bank block (K head-major, V transposed).
+//  unpack         bank block -> token-major K/V (read-out of B_k).
+//
+// Pages cited: [S] "In-Flight KV Cache with Clean Anchors for Faster
+// Autoregressive Video Diffusion", Korean summary page, section "how it
+// works", Eq. (2): the renderer attends its chunk over A_Gamma(i) and B_k^(i)
+// and its own K/V, then B_k^(i+1) = Tail_H(B_k^(i) U (i, K, V)).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <vector>
+
+#include "../ff_internal.h"
+
+namespace ff {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Lazy rescale threshold (base-2 units): the running max is only raised when
+// a tile exceeds it by more than this, so p = 2^(s - m) stays <= 2^8.
+constexpr float kRescaleTau = 8.0f;
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Index of the key source holding virtual key v (v < L_k).
+__device__ __forceinline__ int seg_of(const SegTable& t, int v) {
+  int s = 0;
+  while (s + 1 < t.nseg && v >= t.start[s + 1]) ++s;
+  return s;
+}
+
+// --------------------------------------------------------------------------
+// Segmented attention, bf16 in, fp32 accumulate.
+//
+// Work item = (pair, head, key split, 128-query tile); 4 waves x 32 queries.
+// Per 64-key tile:
+//   S^T[key][q] = sum_d K[key][d] Q[q][d]     (A = K rows from LDS, B = Q regs)
+//   p = 2^(s*scale*log2e - m)                 (per query = per lane column)
+//   O^T[d][q] += sum_key V^T[d][key] P^T[key][q]  (A = V^T from LDS, B = P regs)
+// MFMA 32x32x16 operand layout: lane l holds A[l%32][8*(l/32)..+7] and
+// B[8*(l/32)..+7][l%32]; D[i][l%32] for i = 8*(r/4) + 4*(l/32) + r%4, r < 16.
+// The K rows fed to S^T are permuted (bits 2 and 3 of the row swapped) so
+// that accumulator registers 8*j..8*j+7 of lane l are keys 16*j + 8*(l/32) +
+// 0..7: P leaves the first MFMA already in B-operand order for the second,
+// and V^T rows are read as one contiguous 16-byte run per lane.
+// --------------------------------------------------------------------------
+template <int D>
+struct TileCfg {
+  static constexpr int kKBytes = kBlockN * D * 2;     // K tile [64][D]
+  static constexpr int kVBytes = D * kBlockN * 2;     // V^T tile [D][64]
+  static constexpr int kBufBytes = kKBytes + kVBytes;
+  static constexpr int kKLoads = kBlockN * (D / 8) / 256;   // 16-byte loads per thread
+  static constexpr int kVLoads = D * 8 / 256;
+};
+
+__device__ __forceinline__ int krow_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
+
+template <int D>
+__device__ __forceinline__ void load_tile(const PairLaunch& P, int h, int nh, int v0, int tid,
+                                          u32x4 (&kr)[TileCfg<D>::kKLoads], u32x4 (&vr)[TileCfg<D>::kVLoads]) {
+  const SegTable& t = P.seg;
+  const int lk = P.lk;
+  // Tiles that lie inside one source (all but a handful) take the uniform path.
+  const int s0 = seg_of(t, v0);
+  const int s_end = t.start[s0 + 1];
+  const bool uniform = (v0 + kBlockN <= s_end) || (s_end == lk);
+  const int r0 = tid >> 3, c0 = tid & 7;
+#pragma unroll
+  for (int i = 0; i < TileCfg<D>::kKLoads; ++i) {
+    const int r = r0 + 32 * (i & 1), c = c0 + 8 * (i >> 1);
+    const int v = v0 + r;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (v < lk) {
+      const int s = uniform ? s0 : seg_of(t, v);
+      const int n = t.n[s];
+      const __bf16* kb = static_cast<const __bf16*>(t.base[s]);
+      val = ld16(kb + (int64_t(h) * n + (v - t.start[s])) * D + 8 * c);
+    }
+    kr[i] = val;
+  }
+  {
+    const int v = v0 + 8 * c0;
+    int s = s0, n = 0, off = 0;
+    const __bf16* vb = nullptr;
+    if (v < lk) {
+      s = uniform ? s0 : seg_of(t, v);
+      n = t.n[s];
+      off = v - t.start[s];
+      vb = static_cast<const __bf16*>(t.base[s]) + int64_t(nh) * n * D;
+    }
+#pragma unroll
+    for (int i = 0; i < TileCfg<D>::kVLoads; ++i) {
+      const int dd = r0 + 32 * i;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (v < lk) val = ld16(vb + (int64_t(h) * D + dd) * n + off);
+      vr[i] = val;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(uint8_t* buf, int tid, const u32x4 (&kr)[TileCfg<D>::kKLoads],
+                                           const u32x4 (&vr)[TileCfg<D>::kVLoads]) {
+  const int r0 = tid >> 3, c0 = tid & 7;
+#pragma unroll
+  for (int i = 0; i < TileCfg<D>::kKLoads; ++i) {
+    const int r = r0 + 32 * (i & 1), c = c0 + 8 * (i >> 1);
+    st16(buf + r * (D * 2) + ((c ^ krow_swz(r)) << 4), kr[i]);
+  }
+  uint8_t* vbuf = buf + TileCfg<D>::kKBytes;
+#pragma unroll
+  for (int i = 0; i < TileCfg<D>::kVLoads; ++i) {
+    const int dd = r0 + 32 * i;
+    st16(vbuf + dd * (kBlockN * 2) + ((c0 ^ (dd & 7)) << 4), vr[i]);
+  }
+}
+
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+  // range of work items so that query tiles sharing a head's K/V share an L2.
+  const int x = b & 7, idx = b >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return x * per + (x < rem ? x : rem) + idx;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnLaunch a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TileCfg<D>::kBufBytes];
+  constexpr int KS = D / 16;       // MFMA k-steps over head_dim
+  constexpr int DB = D / 32;       // 32-row blocks of O^T
+
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  int p = 0;
+  while (p + 1 < a.n_pairs && item >= a.pair[p + 1].item_base) ++p;
+  const PairLaunch& P = a.pair[p];
+  const int nh = a.nh, lq = a.lq;
+  int local = item - P.item_base;
+  const int qt = local % a.n_qtiles;
+  local /= a.n_qtiles;
+  const int h = local % nh;
+  const int split = local / nh;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int q = qt * kBlockM + w * 32 + l32;
+  const bool q_ok = q < lq;
+
+  // Q^T as the B operand: lane holds Q[q][16*ks + 8*hl .. +7].
+  bf16x8 qreg[KS];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(P.q) + (int64_t(q) * nh + h) * D + 8 * hl;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q_ok) v = ld16(qp + 16 * ks);
+      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const int ntiles = (P.lk + kBlockN - 1) / kBlockN;
+  const int t_begin = split * P.tiles_per_split;
+  const int t_end = min(ntiles, t_begin + P.tiles_per_split);
+  const float c = a.scale * kLog2e;
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // Row of the K tile this lane feeds as A operand (bits 2 and 3 swapped).
+  const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+
+  u32x4 kr[TileCfg<D>::kKLoads], vr[TileCfg<D>::kVLoads];
+  load_tile<D>(P, h, nh, t_begin * kBlockN, tid, kr, vr);
+  store_tile<D>(lds, tid, kr, vr);
+  __syncthreads();
+
+  for (int t = t_begin; t < t_end; ++t) {
+    uint8_t* buf = lds + ((t - t_begin) & 1) * TileCfg<D>::kBufBytes;
+    const bool more = t + 1 < t_end;
+    if (more) load_tile<D>(P, h, nh, (t + 1) * kBlockN, tid, kr, vr);
+
+    // ---- S^T = K Q^T for two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+      const int row = 32 * kb + prow;
+      const uint8_t* kbase = buf + row * (D * 2);
+      const int sw = krow_swz(row);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = 2 * ks + hl;
+        const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(kbase + ((ch ^ sw) << 4)));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], s[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- mask keys past L_k (last tile only)
+    const int v0 = t * kBlockN;
+    if (v0 + kBlockN > P.lk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = v0 + 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
+          if (key >= P.lk) s[kb][r] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax (base 2), lazy rescale
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mx2 = mx * c;
+    if (__ballot(mx2 > m_run + kRescaleTau)) {
+      const float m_new = fmaxf(m_run, mx2);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * j + e], c, -m_run));
+          l_run += pv;
+          pb[kb][j][e] = (__bf16)pv;
+        }
+
+    // ---- O^T += V^T P^T
+    const uint8_t* vbase = buf + TileCfg<D>::kKBytes;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ch = 4 * kb + 2 * j + hl;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int dd = 32 * db + l32;
+          const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ (dd & 7)) << 4)));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][j], o[db], 0, 0, 0);
+        }
+      }
+
+    if (more) store_tile<D>(lds + (((t - t_begin) & 1) ^ 1) * TileCfg<D>::kBufBytes, tid, kr, vr);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_ok) return;
+  if (P.n_split == 1) {
+    const float inv = 1.0f / l_tot;
+    __bf16* op = static_cast<__bf16*>(P.o) + (int64_t(q) * nh + h) * D + 4 * hl;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[db][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
+      }
+    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (m_run + log2f(l_tot)) * kLn2;
+  } else {
+    float* part = P.part + int64_t(split) * a.part_stride;
+    float* op = part + (int64_t(q) * nh + h) * D + 4 * hl;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float4 ov = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * g) = ov;
+      }
+    if (hl == 0) {
+      float* ml = part + a.part_ml_off + (int64_t(h) * lq + q) * 2;
+      ml[0] = m_run;
+      ml[1] = l_tot;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Split merge: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One thread per (pair, query, head, 4 head-dim values).
+// --------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits_kernel(const AttnLaunch a) {
+  const int64_t per_pair = int64_t(a.lq) * a.nh * (D / 4);
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int p = blockIdx.y;
+  const PairLaunch& P = a.pair[p];
+  if (P.n_split <= 1 || gid >= per_pair) return;
+  const int d4 = int(gid % (D / 4));
+  const int64_t row = gid / (D / 4);            // q * nh + h
+  const int h = int(row % a.nh);
+  const int q = int(row / a.nh);
+  float M = -INFINITY;
+  for (int s = 0; s < P.n_split; ++s)
+    M = fmaxf(M, P.part[s * a.part_stride + a.part_ml_off + (int64_t(h) * a.lq + q) * 2]);
+  float L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < P.n_split; ++s) {
+    const float* part = P.part + s * a.part_stride;
+    const float* ml = part + a.part_ml_off + (int64_t(h) * a.lq + q) * 2;
+    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
+    L += wgt * ml[1];
+    const float4 ov = *reinterpret_cast<const float4*>(part + row * D + 4 * d4);
+    acc.x += wgt * ov.x; acc.y += wgt * ov.y; acc.z += wgt * ov.z; acc.w += wgt * ov.w;
+  }
+  const float inv = 1.0f / L;
+  bf16x4 out;
+  out[0] = (__bf16)(acc.x * inv); out[1] = (__bf16)(acc.y * inv);
+  out[2] = (__bf16)(acc.z * inv); out[3] = (__bf16)(acc.w * inv);
+  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + row * D + 4 * d4) = out;
+  if (P.lse && d4 == 0) P.lse[int64_t(h) * a.lq + q] = (M + log2f(L)) * kLn2;
+}
+
+// --------------------------------------------------------------------------
+// fp32 path: one lane per (pair, query, head); keys streamed in order.
+// --------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const AttnLaunch a) {
+  const int p = blockIdx.y;
+  const PairLaunch& P = a.pair[p];
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (gid >= int64_t(a.lq) * a.nh) return;
+  const int h = int(gid % a.nh), q = int(gid / a.nh);
+  const int nh = a.nh;
+  const float* qp = static_cast<const float*>(P.q) + gid * D;
+  float qv[D], acc[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) { qv[e] = qp[e]; acc[e] = 0.f; }
+  const float c = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  for (int s = 0; s < P.seg.nseg; ++s) {
+    const int n = P.seg.n[s];
+    const float* kb = static_cast<const float*>(P.seg.base[s]) + int64_t(h) * n * D;
+    const float* vb = static_cast<const float*>(P.seg.base[s]) + int64_t(nh) * n * D + int64_t(h) * D * n;
+    for (int j = 0; j < n; ++j) {
+      float dot = 0.f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) dot = fmaf(qv[e], kb[int64_t(j) * D + e], dot);
+      const float sc = dot * c;
+      if (sc > m) {
+        const float alpha = __builtin_amdgcn_exp2f(m - sc);
+        l *= alpha;
+#pragma unroll
+        for (int e = 0; e < D; ++e) acc[e] *= alpha;
+        m = sc;
+      }
+      const float pv = __builtin_amdgcn_exp2f(sc - m);
+      l += pv;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(pv, vb[int64_t(e) * n + j], acc[e]);
+    }
+  }
+  float* op = static_cast<float*>(P.o) + gid * D;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
+  if (P.lse) P.lse[int64_t(h) * a.lq + q] = (m + log2f(l)) * kLn2;
+}
+
+// --------------------------------------------------------------------------
+// Publish (rows -> bank block) and unpack (bank block -> rows).
+// Block = 64 tokens x 1 head of one source.  K moves as 16-byte chunks; V goes
+// through LDS for the [token][d] <-> [d][token] transpose.
+// --------------------------------------------------------------------------
+template <typename E, int D, bool kPublish>
+__global__ __launch_bounds__(256) void layout_copy_kernel(const CopyLaunch cl) {
+  constexpr int EPC = 16 / sizeof(E);             // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;                    // chunks per token row
+  constexpr int TB = 64;                          // tokens per block
+  constexpr int PAD = 1;                          // row padding (elements)
+  __shared__ E tile[TB][D + PAD];
+
+  const int job = blockIdx.z, g = blockIdx.y;
+  if (job >= cl.n_jobs) return;
+  const CopyJob& J = cl.job[job];
+  if (g >= J.nseg) return;
+  const int nh = cl.nh, L = cl.L;
+  const int h = blockIdx.x % nh;
+  const int t0 = (blockIdx.x / nh) * TB;
+  if (t0 >= L) return;
+  const int nt = min(TB, L - t0);                 // multiple of EPC
+  const int tid = threadIdx.x;
+
+  uint8_t* blk = static_cast<uint8_t*>(J.block) + int64_t(g) * cl.block_stride;
+  E* bk = reinterpret_cast<E*>(blk) + (int64_t(h) * L + t0) * D;               // K [h][t][d]
+  E* bv = reinterpret_cast<E*>(blk) + int64_t(nh) * L * D + int64_t(h) * D * L + t0;  // V^T [h][d][t]
+  const int64_t row0 = int64_t(g) * L + t0;      // first token row of this block
+
+  if (kPublish) {
+    const E* rk = static_cast<const E*>(J.rows_k);
+    const E* rv = static_cast<const E*>(J.rows_v);
+    for (int i = tid; i < nt * CPR; i += 256) {
+      const int t = i / CPR, ch = i % CPR;
+      const int64_t src = ((row0 + t) * nh + h) * D + ch * EPC;
+      st16(bk + int64_t(t) * D + ch * EPC, ld16(rk + src));
+      const u32x4 v = ld16(rv + src);
+      const E* ve = reinterpret_cast<const E*>(&v);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) tile[t][ch * EPC + e] = ve[e];
+    }
+    __syncthreads();
+    const int tch = nt / EPC;                       // token chunks per d-row
+    for (int i = tid; i < D * tch; i += 256) {
+      const int dd = i / tch, tc = i % tch;
+      u32x4 v;
+      E* ve = reinterpret_cast<E*>(&v);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) ve[e] = tile[tc * EPC + e][dd];
+      st16(bv + int64_t(dd) * L + tc * EPC, v);
+    }
+  } else {
+    E* ok = static_cast<E*>(J.out_k);
+    E* ov = static_cast<E*>(J.out_v);
+    const int tch = nt / EPC;
+    if (ov) {
+      for (int i = tid; i < D * tch; i += 256) {
+        const int dd = i / tch, tc = i % tch;
+        const u32x4 v = ld16(bv + int64_t(dd) * L + tc * EPC);
+        const E* ve = reinterpret_cast<const E*>(&v);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) tile[tc * EPC + e][dd] = ve[e];
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nt * CPR; i += 256) {
+      const int t = i / CPR, ch = i % CPR;
+      const int64_t dst = ((int64_t(t0) + t) * nh + h) * D + ch * EPC;
+      if (ok) st16(ok + dst, ld16(bk + int64_t(t) * D + ch * EPC));
+      if (ov) {
+        u32x4 v;
+        E* ve = reinterpret_cast<E*>(&v);
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) ve[e] = tile[t][ch * EPC + e];
+        st16(ov + dst, v);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// --------------------------------------------------------------------------
+// Profiler: start/stop event pairs per launch, summed on read.
+// --------------------------------------------------------------------------
+struct Profiler {
+  struct Rec { int kind; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  int64_t count[4] = {0, 0, 0, 0};
+  double ms[4] = {0, 0, 0, 0};
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+
+namespace {
+enum { kAttn = 0, kMerge = 1, kPublish = 2, kAnchor = 3 };
+
+struct Timed {
+  Profiler* p; int kind; hipStream_t s; hipEvent_t a = nullptr, b = nullptr;
+  Timed(Profiler* p_, int k, hipStream_t s_) : p(p_), kind(k), s(s_) {
+    if (p) { a = p->get(); b = p->get(); if (a) (void)hipEventRecord(a, s); }
+  }
+  ~Timed() {
+    if (p && a && b) { (void)hipEventRecord(b, s); p->pending.push_back({kind, a, b}); }
+  }
+};
+
+int launch_ok() {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    std::fprintf(stderr, "ff: kernel launch failed: %s\n", hipGetErrorString(e));
+    return FF_E_HIP;
+  }
+  return 0;
+}
+}  // namespace
+
+int dev_launch_attention(const AttnLaunch& a, void* stream, Profiler* prof) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (a.dtype == FF_F32) {
+    Timed tm(prof, kAttn, s);
+    dim3 grid(unsigned((int64_t(a.lq) * a.nh + 63) / 64), unsigned(a.n_pairs));
+    if (a.d == 64) hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, a);
+    return launch_ok();
+  }
+  {
+    Timed tm(prof, kAttn, s);
+    if (a.d == 64) hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(a.total_items), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(a.total_items), dim3(256), 0, s, a);
+  }
+  if (launch_ok()) return FF_E_HIP;
+  bool any_split = false;
+  for (int p = 0; p < a.n_pairs; ++p) any_split |= a.pair[p].n_split > 1;
+  if (any_split) {
+    Timed tm(prof, kMerge, s);
+    const int64_t n = int64_t(a.lq) * a.nh * (a.d / 4);
+    dim3 grid(unsigned((n + 255) / 256), unsigned(a.n_pairs));
+    if (a.d == 64) hipLaunchKernelGGL(merge_splits_kernel<64>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(merge_splits_kernel<128>, grid, dim3(256), 0, s, a);
+    return launch_ok();
+  }
+  return 0;
+}
+
+template <bool kPublish>
+static void launch_copy(const CopyLaunch& c, hipStream_t s) {
+  dim3 grid(unsigned(((c.L + 63) / 64) * c.nh), unsigned(c.max_nseg), unsigned(c.n_jobs));
+  if (c.dtype == FF_F32) {
+    if (c.d == 64) hipLaunchKernelGGL((layout_copy_kernel<float, 64, kPublish>), grid, dim3(256), 0, s, c);
+    else hipLaunchKernelGGL((layout_copy_kernel<float, 128, kPublish>), grid, dim3(256), 0, s, c);
+  } else {
+    if (c.d == 64) hipLaunchKernelGGL((layout_copy_kernel<uint16_t, 64, kPublish>), grid, dim3(256), 0, s, c);
+    else hipLaunchKernelGGL((layout_copy_kernel<uint16_t, 128, kPublish>), grid, dim3(256), 0, s, c);
+  }
+}
+
+int dev_launch_publish(const CopyLaunch& c, void* stream, Profiler* prof, bool anchor) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  {
+    Timed tm(prof, anchor ? kAnchor : kPublish, s);
+    launch_copy<true>(c, s);
+  }
+  return launch_ok();
+}
+
+int dev_launch_unpack(const CopyLaunch& c, void* stream) {
+  launch_copy<false>(c, static_cast<hipStream_t>(stream));
+  return launch_ok();
+}
+
+Profiler* dev_profiler_create() { return new Profiler(); }
+
+void dev_profiler_destroy(Profiler* p) {
+  if (!p) return;
+  for (auto& r : p->pending) { (void)hipEventDestroy(r.a); (void)hipEventDestroy(r.b); }
+  for (auto e : p->pool) (void)hipEventDestroy(e);
+  delete p;
+}
+
+void dev_profiler_reset(Profiler* p) {
+  if (!p) return;
+  for (auto& r : p->pending) {
+    (void)hipEventSynchronize(r.b);
+    p->pool.push_back(r.a);
+    p->pool.push_back(r.b);
+  }
+  p->pending.clear();
+  for (int k = 0; k < 4; ++k) { p->count[k] = 0; p->ms[k] = 0; }
+}
+
+int dev_profiler_read(Profiler* p, ff_kernel_times* out) {
+  int rc = 0;
+  for (auto& r : p->pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) rc = FF_E_HIP;
+    p->count[r.kind] += 1;
+    p->ms[r.kind] += ms;
+    p->pool.push_back(r.a);
+    p->pool.push_back(r.b);
+  }
+  p->pending.clear();
+  out->attn_launches = p->count[kAttn];     out->attn_ms = p->ms[kAttn];
+  out->merge_launches = p->count[kMerge];   out->merge_ms = p->ms[kMerge];
+  out->publish_launches = p->count[kPublish]; out->publish_ms = p->ms[kPublish];
+  out->anchor_launches = p->count[kAnchor]; out->anchor_ms = p->ms[kAnchor];
+  return rc;
+}
+
+}  // namespace ff

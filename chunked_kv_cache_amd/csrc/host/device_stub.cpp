@@ -1,0 +1,75 @@
+// Recording stand-in for the device launchers, linked only into the host-check
+// library (libff_hostcheck.so) that CPU tests load to exercise the C ABI's
+// bookkeeping without a GPU.  Nothing is launched: each call records what it
+// would have launched, and the tests read the record back.
+#include <cstring>
+
+#include "../ff_internal.h"
+
+namespace ff {
+
+struct Profiler {};
+
+namespace {
+AttnLaunch g_last_attn;
+CopyLaunch g_last_copy;
+int g_n_attn = 0, g_n_publish = 0, g_n_anchor = 0, g_n_unpack = 0;
+}  // namespace
+
+int dev_launch_attention(const AttnLaunch& a, void*, Profiler*) {
+  g_last_attn = a;
+  ++g_n_attn;
+  return 0;
+}
+
+int dev_launch_publish(const CopyLaunch& c, void*, Profiler*, bool anchor) {
+  g_last_copy = c;
+  ++(anchor ? g_n_anchor : g_n_publish);
+  return 0;
+}
+
+int dev_launch_unpack(const CopyLaunch& c, void*) {
+  g_last_copy = c;
+  ++g_n_unpack;
+  return 0;
+}
+
+Profiler* dev_profiler_create() { return new Profiler(); }
+void dev_profiler_destroy(Profiler* p) { delete p; }
+void dev_profiler_reset(Profiler*) {}
+int dev_profiler_read(Profiler*, ff_kernel_times* out) {
+  std::memset(out, 0, sizeof(*out));
+  return 0;
+}
+
+}  // namespace ff
+
+// Inspection hooks of the host-check build (not part of ff.h).
+extern "C" {
+void ffstub_counts(int* attn, int* publish, int* anchor, int* unpack) {
+  *attn = ff::g_n_attn;
+  *publish = ff::g_n_publish;
+  *anchor = ff::g_n_anchor;
+  *unpack = ff::g_n_unpack;
+}
+// Key-source table of pair p of the last attention launch, as byte offsets
+// from `ws` and token counts; returns the number of sources.
+int ffstub_last_segments(int p, const void* ws, long long* offsets, int* n_tokens, int* lk, int* n_split) {
+  const ff::PairLaunch& P = ff::g_last_attn.pair[p];
+  for (int s = 0; s < P.seg.nseg; ++s) {
+    offsets[s] = static_cast<const char*>(P.seg.base[s]) - static_cast<const char*>(ws);
+    n_tokens[s] = P.seg.n[s];
+  }
+  *lk = P.lk;
+  *n_split = P.n_split;
+  return P.seg.nseg;
+}
+int ffstub_last_attn_pairs(int* total_items) {
+  *total_items = ff::g_last_attn.total_items;
+  return ff::g_last_attn.n_pairs;
+}
+// Destination block of job j of the last copy launch, as a byte offset from ws.
+long long ffstub_last_copy_block(int j, const void* ws) {
+  return static_cast<const char*>(ff::g_last_copy.job[j].block) - static_cast<const char*>(ws);
+}
+}

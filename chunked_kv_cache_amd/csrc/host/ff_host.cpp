@@ -1,0 +1,430 @@
+// Host side of the C ABI: shape checks, workspace layout, Gamma(i), the
+// stage-bank ring metadata, the key plan of a call, and launch assembly.
+// Plain C++17; all device work goes through the dev_* functions.
+//
+// Pages cited: [S] "In-Flight KV Cache with Clean Anchors for Faster
+// Autoregressive Video Diffusion", Korean summary page ("how it works",
+// Eq. (2); "how it differs"; "what it is").
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../ff_internal.h"
+
+using namespace ff;
+
+struct ff_ctx {
+  ff_shape shape;
+  int S = 0, H = 0;
+  int n_anchor = 0, n_chunk = 0;
+  int64_t T = 0, Lq = 0;          // tokens per latent, tokens per chunk
+  int64_t esz = 2;
+  uint8_t* ws = nullptr;
+  size_t ws_bytes = 0;
+  // workspace regions (byte offsets from ws)
+  size_t anchor_off = 0, anchor_block = 0;   // anchor a: anchor_off + a*anchor_block
+  size_t slot_off = 0, slot_block = 0;       // stage k, slot s: slot_off + (k*(H+1)+s)*slot_block
+  size_t part_off = 0, part_bytes_per_split = 0;
+  // metadata
+  std::vector<uint8_t> anchor_present;
+  std::vector<int> next;                     // next chunk per stage
+  std::vector<uint8_t> can_rewind;
+  Profiler* prof = nullptr;
+  bool profiling = false;
+};
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool shape_ok(const ff_shape* s, int S, int H) {
+  if (!s) return false;
+  if (s->n_heads < 1 || s->n_heads > 1024) return false;
+  if (s->head_dim != 64 && s->head_dim != 128) return false;
+  if (s->tokens_per_latent < 8 || s->tokens_per_latent % 8 || s->tokens_per_latent > (1 << 20)) return false;
+  if (s->chunk_latents < 1 || s->anchor_stride < 1) return false;
+  // At most 3 anchors per chunk under either rule needs B_R <= Delta.
+  if (s->chunk_latents > s->anchor_stride) return false;
+  if (s->n_latents < s->chunk_latents || s->n_latents % s->chunk_latents) return false;
+  if (s->w_ctx < 1) return false;
+  if (s->dtype != FF_BF16 && s->dtype != FF_F32) return false;
+  if (s->gamma_rule != FF_GAMMA_BRACKET && s->gamma_rule != FF_GAMMA_CENTER_LR) return false;
+  if (S < 1 || S > 64 || H < 1 || H > kMaxHistory) return false;
+  // query rows per chunk times heads must index in 32 bits
+  const int64_t lq = int64_t(s->chunk_latents) * s->tokens_per_latent;
+  if (lq * s->n_heads * s->head_dim > (int64_t(1) << 31) - 1) return false;
+  return true;
+}
+
+struct Layout {
+  size_t anchor_off, anchor_block, slot_off, slot_block, part_off, part_per_split, total;
+  int n_anchor, n_chunk;
+};
+
+Layout layout_of(const ff_shape* s, int S, int H) {
+  Layout L{};
+  const size_t esz = s->dtype == FF_F32 ? 4 : 2;
+  const size_t T = size_t(s->tokens_per_latent), nh = size_t(s->n_heads), d = size_t(s->head_dim);
+  const size_t lq = T * size_t(s->chunk_latents);
+  L.n_anchor = (s->n_latents + s->anchor_stride - 1) / s->anchor_stride;
+  L.n_chunk = s->n_latents / s->chunk_latents;
+  L.anchor_block = align_up(2 * nh * T * d * esz);
+  L.slot_block = align_up(2 * nh * lq * d * esz);
+  L.anchor_off = 0;
+  L.slot_off = L.anchor_off + size_t(L.n_anchor) * L.anchor_block;
+  L.part_per_split = align_up(lq * nh * d * 4) + align_up(nh * lq * 2 * 4);
+  L.part_off = L.slot_off + size_t(S) * size_t(H + 1) * L.slot_block;
+  L.total = L.part_off + size_t(kMaxSplit) * L.part_per_split;
+  return L;
+}
+
+// Gamma(i): reading of [S] "how it differs" / "how it is used" (see ff.h).
+int gamma_of(const ff_ctx* c, int i, int* ids) {
+  const int D = c->shape.anchor_stride, B = c->shape.chunk_latents;
+  const int p0 = B * i, p1 = B * i + B - 1;
+  int n = 0;
+  if (c->shape.gamma_rule == FF_GAMMA_BRACKET) {
+    const int lo = (p0 / D) * D, hi = ((p1 + D - 1) / D) * D;
+    for (int a = lo / D; a <= hi / D && a < c->n_anchor; ++a) ids[n++] = a;
+  } else {
+    const int left = (p0 + B / 2) / D;
+    for (int a = left; a <= left + 1 && a < c->n_anchor; ++a) ids[n++] = a;
+  }
+  return n;
+}
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool lse_ok(const float* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+uint8_t* slot_ptr(const ff_ctx* c, int stage, int chunk) {
+  const int s = chunk % (c->H + 1);
+  return c->ws + c->slot_off + (size_t(stage) * size_t(c->H + 1) + size_t(s)) * c->slot_block;
+}
+
+// Order contract of one call against the current state (no side effects).
+ff_status check_call(const ff_ctx* c, int i, int k) {
+  if (k < 0 || k >= c->S || i < 0 || i >= c->n_chunk) return FF_E_RANGE;
+  if (c->next[k] != i) return FF_E_ORDER;
+  if (k > 0 && c->next[k - 1] <= i) return FF_E_ORDER;
+  int ids[8];
+  const int n = gamma_of(c, i, ids);
+  for (int j = 0; j < n; ++j)
+    if (!c->anchor_present[ids[j]]) return FF_E_ANCHOR_MISSING;
+  return FF_OK;
+}
+
+// Key sources of (i, k): Gamma(i) anchors ascending, then B_k^(i) oldest
+// first, then the chunk itself; oldest history dropped while over W_ctx.
+void plan_of(const ff_ctx* c, int i, int k, ff_key_sources* p) {
+  std::memset(p, 0, sizeof(*p));
+  int ids[8];
+  const int na = gamma_of(c, i, ids);
+  const int B = c->shape.chunk_latents;
+  int h_first = c->next[k] - std::min(c->next[k], c->H);   // B_k^(i) = [h_first, i)
+  while (h_first < i && na + B * (i - h_first + 1) > c->shape.w_ctx) ++h_first;
+  int n = 0;
+  for (int j = 0; j < na; ++j) {
+    p->kind[n] = FF_SRC_ANCHOR; p->id[n] = ids[j]; p->n_tokens[n] = int32_t(c->T); ++n;
+  }
+  for (int ch = h_first; ch < i; ++ch) {
+    p->kind[n] = FF_SRC_HISTORY; p->id[n] = ch; p->n_tokens[n] = int32_t(c->Lq); ++n;
+  }
+  p->kind[n] = FF_SRC_OWN; p->id[n] = i; p->n_tokens[n] = int32_t(c->Lq); ++n;
+  p->n_sources = n;
+  p->key_latents = na + B * (i - h_first + 1);
+  int64_t tot = 0;
+  for (int j = 0; j < n; ++j) tot += p->n_tokens[j];
+  p->key_tokens = int32_t(tot);
+}
+
+void seg_table_of(const ff_ctx* c, int k, const ff_key_sources& p, SegTable* t) {
+  std::memset(t, 0, sizeof(*t));
+  int32_t acc = 0;
+  for (int j = 0; j < p.n_sources; ++j) {
+    const uint8_t* base = p.kind[j] == FF_SRC_ANCHOR
+                              ? c->ws + c->anchor_off + size_t(p.id[j]) * c->anchor_block
+                              : slot_ptr(c, k, p.id[j]);
+    t->base[j] = base;
+    t->n[j] = p.n_tokens[j];
+    t->start[j] = acc;
+    acc += p.n_tokens[j];
+  }
+  t->start[p.n_sources] = acc;
+  t->nseg = p.n_sources;
+}
+
+// Work decomposition: items = heads x query tiles (x key splits).  Splits
+// are used only when the unsplit grid would leave most of the chip idle.
+void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_sources* plans,
+                    const void* const* Q, void* const* O, float* const* lse, AttnLaunch* a) {
+  std::memset(a, 0, sizeof(*a));
+  a->n_pairs = n_pairs;
+  a->nh = c->shape.n_heads;
+  a->d = c->shape.head_dim;
+  a->lq = int32_t(c->Lq);
+  a->n_qtiles = int32_t((c->Lq + kBlockM - 1) / kBlockM);
+  a->dtype = c->shape.dtype;
+  a->scale = float(1.0 / std::sqrt(double(c->shape.head_dim)));
+  a->part_stride = int64_t(c->part_bytes_per_split / 4);
+  a->part_ml_off = int64_t(align_up(size_t(c->Lq) * size_t(a->nh) * size_t(a->d) * 4) / 4);
+  const int64_t items1 = int64_t(a->nh) * a->n_qtiles * n_pairs;
+  int split = 1;
+  if (c->shape.dtype == FF_BF16) {
+    while (split * 2 * n_pairs <= kMaxSplit && items1 * split < 480) split *= 2;
+  }
+  int32_t base = 0;
+  for (int p = 0; p < n_pairs; ++p) {
+    PairLaunch& pl = a->pair[p];
+    pl.q = Q[p];
+    pl.o = O[p];
+    pl.lse = lse ? lse[p] : nullptr;
+    seg_table_of(c, ks[p], plans[p], &pl.seg);
+    pl.lk = plans[p].key_tokens;
+    const int ntiles = (pl.lk + kBlockN - 1) / kBlockN;
+    int sp = std::min(split, ntiles);
+    pl.tiles_per_split = (ntiles + sp - 1) / sp;
+    sp = (ntiles + pl.tiles_per_split - 1) / pl.tiles_per_split;   // no empty split
+    pl.n_split = sp;
+    pl.part = sp > 1 ? reinterpret_cast<float*>(c->ws + c->part_off + size_t(p) * split * c->part_bytes_per_split)
+                     : nullptr;
+    pl.item_base = base;
+    base += a->nh * a->n_qtiles * sp;
+  }
+  a->total_items = base;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ff_status_str(ff_status s) {
+  switch (s) {
+    case FF_OK: return "ok";
+    case FF_E_INVAL: return "invalid argument (null/misaligned pointer or unsupported shape)";
+    case FF_E_ORDER: return "order contract violated (not the next chunk of this stage, or previous stage not run)";
+    case FF_E_ANCHOR_MISSING: return "an anchor of Gamma(i) has not been published";
+    case FF_E_ANCHOR_EXISTS: return "anchor already published (anchor bank is append-only)";
+    case FF_E_RANGE: return "chunk, stage or anchor id out of range";
+    case FF_E_NOSPACE: return "workspace smaller than ff_workspace_bytes()";
+    case FF_E_HIP: return "HIP runtime call failed";
+    case FF_E_STATE: return "operation not possible in the current state";
+  }
+  return "unknown status";
+}
+
+size_t ff_workspace_bytes(const ff_shape* shape, int n_stages, int history) {
+  if (!shape_ok(shape, n_stages, history)) return 0;
+  return layout_of(shape, n_stages, history).total;
+}
+
+ff_status ff_stage_bank_create(const ff_shape* shape, int n_stages, int history, void* workspace,
+                               size_t workspace_bytes, ff_ctx** out) {
+  if (!out) return FF_E_INVAL;
+  *out = nullptr;
+  if (!shape_ok(shape, n_stages, history)) return FF_E_INVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))) return FF_E_INVAL;
+  const Layout L = layout_of(shape, n_stages, history);
+  if (workspace_bytes < L.total) return FF_E_NOSPACE;
+  ff_ctx* c = new (std::nothrow) ff_ctx();
+  if (!c) return FF_E_INVAL;
+  c->shape = *shape;
+  c->S = n_stages;
+  c->H = history;
+  c->n_anchor = L.n_anchor;
+  c->n_chunk = L.n_chunk;
+  c->T = shape->tokens_per_latent;
+  c->Lq = int64_t(shape->tokens_per_latent) * shape->chunk_latents;
+  c->esz = elem_size(shape->dtype);
+  c->ws = static_cast<uint8_t*>(workspace);
+  c->ws_bytes = workspace_bytes;
+  c->anchor_off = L.anchor_off;
+  c->anchor_block = L.anchor_block;
+  c->slot_off = L.slot_off;
+  c->slot_block = L.slot_block;
+  c->part_off = L.part_off;
+  c->part_bytes_per_split = L.part_per_split;
+  c->anchor_present.assign(size_t(L.n_anchor), 0);
+  c->next.assign(size_t(n_stages), 0);
+  c->can_rewind.assign(size_t(n_stages), 0);
+  *out = c;
+  return FF_OK;
+}
+
+void ff_destroy(ff_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->prof) dev_profiler_destroy(ctx->prof);
+  delete ctx;
+}
+
+ff_status ff_anchor_bank_publish(ff_ctx* c, int first_anchor, int n_anchors, const void* K, const void* V,
+                                 void* stream) {
+  if (!c || !aligned16(K) || !aligned16(V)) return FF_E_INVAL;
+  if (n_anchors < 1 || first_anchor < 0 || first_anchor > c->n_anchor - n_anchors) return FF_E_RANGE;
+  for (int a = first_anchor; a < first_anchor + n_anchors; ++a)
+    if (c->anchor_present[a]) return FF_E_ANCHOR_EXISTS;
+  CopyLaunch cl;
+  std::memset(&cl, 0, sizeof(cl));
+  cl.n_jobs = 1;
+  cl.max_nseg = n_anchors;
+  cl.L = int32_t(c->T);
+  cl.nh = c->shape.n_heads;
+  cl.d = c->shape.head_dim;
+  cl.dtype = c->shape.dtype;
+  cl.block_stride = int64_t(c->anchor_block);
+  cl.job[0].rows_k = K;
+  cl.job[0].rows_v = V;
+  cl.job[0].block = c->ws + c->anchor_off + size_t(first_anchor) * c->anchor_block;
+  cl.job[0].nseg = n_anchors;
+  if (dev_launch_publish(cl, stream, c->profiling ? c->prof : nullptr, true) != 0) return FF_E_HIP;
+  for (int a = first_anchor; a < first_anchor + n_anchors; ++a) c->anchor_present[a] = 1;
+  return FF_OK;
+}
+
+ff_status ff_render_attend_grouped(ff_ctx* c, int n_pairs, const int* chunks, const int* stages,
+                                   const void* const* Q, const void* const* K, const void* const* V,
+                                   void* const* O, float* const* lse, void* stream) {
+  if (!c || !chunks || !stages || !Q || !K || !V || !O) return FF_E_INVAL;
+  if (n_pairs < 1 || n_pairs > kMaxPairs) return FF_E_INVAL;
+  for (int p = 0; p < n_pairs; ++p) {
+    if (!aligned16(Q[p]) || !aligned16(K[p]) || !aligned16(V[p]) || !aligned16(O[p])) return FF_E_INVAL;
+    if (lse && !lse_ok(lse[p])) return FF_E_INVAL;
+  }
+  for (int p = 0; p < n_pairs; ++p) {
+    const ff_status st = check_call(c, chunks[p], stages[p]);
+    if (st != FF_OK) return st;
+    for (int q = 0; q < p; ++q)
+      if (stages[q] == stages[p]) return FF_E_ORDER;
+  }
+  ff_key_sources plans[kMaxPairs];
+  for (int p = 0; p < n_pairs; ++p) plan_of(c, chunks[p], stages[p], &plans[p]);
+
+  // 1) Tail_H publish of every pair's in-flight K/V into slot i mod (H+1).
+  //    That slot holds chunk i-H-1, which no pair of this call reads.
+  CopyLaunch cl;
+  std::memset(&cl, 0, sizeof(cl));
+  cl.n_jobs = n_pairs;
+  cl.max_nseg = 1;
+  cl.L = int32_t(c->Lq);
+  cl.nh = c->shape.n_heads;
+  cl.d = c->shape.head_dim;
+  cl.dtype = c->shape.dtype;
+  cl.block_stride = int64_t(c->slot_block);
+  for (int p = 0; p < n_pairs; ++p) {
+    cl.job[p].rows_k = K[p];
+    cl.job[p].rows_v = V[p];
+    cl.job[p].block = slot_ptr(c, stages[p], chunks[p]);
+    cl.job[p].nseg = 1;
+  }
+  Profiler* prof = c->profiling ? c->prof : nullptr;
+  if (dev_launch_publish(cl, stream, prof, false) != 0) return FF_E_HIP;
+
+  // 2) Segmented attention over anchors + history + own (now in the bank).
+  AttnLaunch al;
+  fill_attention(c, n_pairs, stages, plans, Q, O, lse, &al);
+  if (dev_launch_attention(al, stream, prof) != 0) return FF_E_HIP;
+
+  for (int p = 0; p < n_pairs; ++p) {
+    c->next[stages[p]] = chunks[p] + 1;
+    c->can_rewind[stages[p]] = 1;
+  }
+  return FF_OK;
+}
+
+ff_status ff_render_attend(ff_ctx* c, int chunk, int stage, const void* Q, const void* K, const void* V,
+                           void* O, float* lse, void* stream) {
+  const void* q[1] = {Q};
+  const void* k[1] = {K};
+  const void* v[1] = {V};
+  void* o[1] = {O};
+  float* l[1] = {lse};
+  return ff_render_attend_grouped(c, 1, &chunk, &stage, q, k, v, o, l, stream);
+}
+
+ff_status ff_bank_tail(const ff_ctx* c, int stage, int* n_out, int* chunk_ids, void* K_out, void* V_out,
+                       void* stream) {
+  if (!c || !n_out || !chunk_ids) return FF_E_INVAL;
+  if (stage < 0 || stage >= c->S) return FF_E_RANGE;
+  if ((K_out && !aligned16(K_out)) || (V_out && !aligned16(V_out))) return FF_E_INVAL;
+  const int nx = c->next[stage];
+  const int n = std::min(nx, c->H);
+  *n_out = n;
+  for (int j = 0; j < n; ++j) chunk_ids[j] = nx - n + j;
+  if ((!K_out && !V_out) || n == 0) return FF_OK;
+  CopyLaunch cl;
+  std::memset(&cl, 0, sizeof(cl));
+  cl.n_jobs = n;
+  cl.max_nseg = 1;
+  cl.L = int32_t(c->Lq);
+  cl.nh = c->shape.n_heads;
+  cl.d = c->shape.head_dim;
+  cl.dtype = c->shape.dtype;
+  cl.block_stride = int64_t(c->slot_block);
+  const size_t chunk_bytes = size_t(c->Lq) * size_t(c->shape.n_heads) * size_t(c->shape.head_dim) * size_t(c->esz);
+  for (int j = 0; j < n; ++j) {
+    cl.job[j].block = slot_ptr(c, stage, nx - n + j);
+    cl.job[j].out_k = K_out ? static_cast<uint8_t*>(K_out) + size_t(j) * chunk_bytes : nullptr;
+    cl.job[j].out_v = V_out ? static_cast<uint8_t*>(V_out) + size_t(j) * chunk_bytes : nullptr;
+    cl.job[j].nseg = 1;
+  }
+  if (dev_launch_unpack(cl, stream) != 0) return FF_E_HIP;
+  return FF_OK;
+}
+
+ff_status ff_gamma(const ff_ctx* c, int chunk, int* n_out, int* anchor_ids) {
+  if (!c || !n_out || !anchor_ids) return FF_E_INVAL;
+  if (chunk < 0 || chunk >= c->n_chunk) return FF_E_RANGE;
+  int ids[8];
+  const int n = gamma_of(c, chunk, ids);
+  for (int j = 0; j < n; ++j) anchor_ids[j] = ids[j];
+  *n_out = n;
+  return FF_OK;
+}
+
+ff_status ff_key_plan(const ff_ctx* c, int chunk, int stage, ff_key_sources* out) {
+  if (!c || !out) return FF_E_INVAL;
+  const ff_status st = check_call(c, chunk, stage);
+  if (st != FF_OK) return st;
+  plan_of(c, chunk, stage, out);
+  return FF_OK;
+}
+
+ff_status ff_stage_next(const ff_ctx* c, int stage, int* next_chunk) {
+  if (!c || !next_chunk) return FF_E_INVAL;
+  if (stage < 0 || stage >= c->S) return FF_E_RANGE;
+  *next_chunk = c->next[stage];
+  return FF_OK;
+}
+
+ff_status ff_stage_bank_rewind(ff_ctx* c, int stage) {
+  if (!c) return FF_E_INVAL;
+  if (stage < 0 || stage >= c->S) return FF_E_RANGE;
+  if (!c->can_rewind[stage] || c->next[stage] == 0) return FF_E_STATE;
+  const int j = c->next[stage] - 1;
+  if (stage + 1 < c->S && c->next[stage + 1] > j) return FF_E_STATE;
+  c->next[stage] = j;
+  c->can_rewind[stage] = 0;
+  return FF_OK;
+}
+
+ff_status ff_profile_enable(ff_ctx* c, int on) {
+  if (!c) return FF_E_INVAL;
+  if (on && !c->prof) {
+    c->prof = dev_profiler_create();
+    if (!c->prof) return FF_E_HIP;
+  }
+  if (c->prof) dev_profiler_reset(c->prof);
+  c->profiling = on != 0;
+  return FF_OK;
+}
+
+ff_status ff_profile_read(ff_ctx* c, ff_kernel_times* out) {
+  if (!c || !out) return FF_E_INVAL;
+  std::memset(out, 0, sizeof(*out));
+  if (!c->prof) return FF_OK;
+  return dev_profiler_read(c->prof, out) == 0 ? FF_OK : FF_E_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,199 @@
+/*
+ * ff.h -- C ABI of the FlashForward renderer hot path on MI355X (gfx950).
+ *
+ * One renderer call attends a noisy chunk's queries over three key sources at
+ * once -- the clean anchor KV chosen by Gamma(i), the same-stage history bank
+ * B_k (last H chunks) and the chunk's own in-flight K/V -- and publishes that
+ * K/V into B_k by Tail_H, so no cache-update-only forward exists.
+ *
+ * Pages cited:
+ *   [S] "In-Flight KV Cache with Clean Anchors for Faster Autoregressive Video
+ *       Diffusion", Korean summary page: sections "what it is" (무엇인가),
+ *       "how it works" (어떻게 동작하나, Eq. (2)), "how it differs"
+ *       (무엇과 다른가), "how it is used" (어떻게 쓰나).
+ *   [A] the same title, abstract page.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Tensors are token-major [tokens][n_heads][head_dim], contiguous, in the
+ *    context's dtype (bf16 = 2 bytes, f32 = 4 bytes); device pointers are
+ *    caller-owned and must be 16-byte aligned.  `lse` is f32 [n_heads][tokens].
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *    enqueue kernels on it and return without synchronising; buffers must stay
+ *    alive until the stream has passed them.
+ *  - The library allocates no device memory.  All device state (anchor bank,
+ *    stage banks, split-K partials) lives in one caller-owned workspace of
+ *    ff_workspace_bytes() bytes, 256-byte aligned, which must outlive the ctx.
+ *  - Every call validates all arguments and the state contract before it
+ *    enqueues anything.  A call that returns an error other than FF_E_HIP has
+ *    enqueued nothing and changed no state.  FF_E_HIP means a HIP launch
+ *    failed after validation: host metadata is left unchanged, device bank
+ *    bytes of the slot being written are undefined.
+ *  - One context is used by one host thread at a time (no internal locking).
+ */
+#ifndef FF_H_
+#define FF_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FF_OK = 0,
+  FF_E_INVAL = -1,           /* null / misaligned pointer, unsupported shape   */
+  FF_E_ORDER = -2,           /* (i,k) is not the next call of stage k, or      */
+                             /* chunk i has not run stage k-1 yet              */
+  FF_E_ANCHOR_MISSING = -3,  /* an anchor of Gamma(i) is not published         */
+  FF_E_ANCHOR_EXISTS = -4,   /* anchor already published (append-only bank)    */
+  FF_E_RANGE = -5,           /* chunk, stage or anchor id out of range         */
+  FF_E_NOSPACE = -6,         /* workspace smaller than ff_workspace_bytes()    */
+  FF_E_HIP = -7,             /* a HIP runtime call failed                      */
+  FF_E_STATE = -8            /* rewind not possible in the current state       */
+} ff_status;
+
+typedef enum { FF_BF16 = 0, FF_F32 = 1 } ff_dtype;
+
+/* Gamma(i), the anchor selection of chunk i.  [S] "how it differs" / "how it is
+ * used" name it but never write it out; [A] calls the anchors two-sided.
+ *  FF_GAMMA_BRACKET  : every anchor at a position in
+ *                      [Delta*floor(p0/Delta), Delta*ceil(p1/Delta)], p0..p1 the
+ *                      chunk's latent positions (2 anchors, 3 when one lies
+ *                      strictly inside the chunk).  Default.
+ *  FF_GAMMA_CENTER_LR: the anchor at or left of the chunk's middle latent and
+ *                      the next one (always 2 inside the clip).               */
+typedef enum { FF_GAMMA_BRACKET = 0, FF_GAMMA_CENTER_LR = 1 } ff_gamma_rule;
+
+/* Static shape of one attention layer of the renderer.  [S] "how it differs":
+ * B_R = 3 latents per chunk, Delta = 10, W_ctx = 21; 81 latents per clip.    */
+typedef struct {
+  int32_t n_heads;            /* >= 1                                         */
+  int32_t head_dim;           /* 64 or 128                                    */
+  int32_t tokens_per_latent;  /* T >= 8, multiple of 8                        */
+  int32_t chunk_latents;      /* B_R (latents per renderer chunk), >= 1       */
+  int32_t anchor_stride;      /* Delta: anchors at latent positions 0,D,2D..  */
+  int32_t n_latents;          /* clip length, multiple of chunk_latents       */
+  int32_t w_ctx;              /* max key latents per call (oldest history is  */
+                              /* dropped first beyond it)                     */
+  int32_t dtype;              /* ff_dtype                                     */
+  int32_t gamma_rule;         /* ff_gamma_rule                                */
+} ff_shape;
+
+typedef struct ff_ctx ff_ctx;                    /* opaque host-side state    */
+
+/* Key sources of one call, in the order attention sees them. */
+enum { FF_SRC_ANCHOR = 0, FF_SRC_HISTORY = 1, FF_SRC_OWN = 2 };
+#define FF_MAX_SOURCES 16
+typedef struct {
+  int32_t n_sources;
+  int32_t kind[FF_MAX_SOURCES];      /* FF_SRC_*                              */
+  int32_t id[FF_MAX_SOURCES];        /* anchor id or chunk id                 */
+  int32_t n_tokens[FF_MAX_SOURCES];
+  int32_t key_tokens;                /* sum of n_tokens (L_k)                 */
+  int32_t key_latents;
+} ff_key_sources;
+
+/* Accumulated device time per kernel family while profiling is enabled. */
+typedef struct {
+  int64_t attn_launches;    double attn_ms;      /* segmented attention        */
+  int64_t merge_launches;   double merge_ms;     /* split-K LSE merge          */
+  int64_t publish_launches; double publish_ms;   /* Tail_H stage-bank publish  */
+  int64_t anchor_launches;  double anchor_ms;    /* anchor-bank publish        */
+} ff_kernel_times;
+
+/* Bytes of device workspace for a context with n_stages banks of history H.
+ * 0 if the shape is unsupported.  Layout: anchor bank (every anchor of the
+ * clip), S*(H+1) stage-bank slots, split-K partials.                          */
+size_t ff_workspace_bytes(const ff_shape* shape, int n_stages, int history);
+
+/* ff_stage_bank_create -- [S] "how it works", Eq. (2): one history bank B_k
+ * per denoising stage k (S of them) of capacity H, plus the anchor bank A.
+ * Each bank is a ring of H+1 slots so that the publish of chunk i never
+ * overwrites chunk i-H, which the same call still reads.  history <= 8.
+ * On success *out owns only host memory; the workspace stays the caller's.   */
+ff_status ff_stage_bank_create(const ff_shape* shape, int n_stages, int history,
+                               void* workspace, size_t workspace_bytes, ff_ctx** out);
+
+/* Frees the host-side context (not the workspace).  NULL is accepted. */
+void ff_destroy(ff_ctx* ctx);
+
+/* ff_anchor_bank_publish -- [S] "how it differs": after each completed
+ * planner block one cache-extraction forward publishes the block's clean
+ * anchor KV.  K, V: [n_anchors*T][n_heads][head_dim] of anchors
+ * first_anchor .. first_anchor+n_anchors-1 (anchor a sits at latent a*Delta).
+ * Append-only: republishing an anchor is FF_E_ANCHOR_EXISTS.                 */
+ff_status ff_anchor_bank_publish(ff_ctx* ctx, int first_anchor, int n_anchors,
+                                 const void* K, const void* V, void* stream);
+
+/* ff_render_attend -- [S] "how it works", Eq. (2):
+ *   (v_hat, K, V) = F_R(x, c, tau_k; A_Gamma(i), B_k^(i)),
+ *   B_k^(i+1)     = Tail_H(B_k^(i) U (i, K, V)).
+ * Q, K, V: the chunk's in-flight projections, [B_R*T][n_heads][head_dim].
+ * O: same shape, O = softmax(Q K_all^T / sqrt(d)) V_all over the keys of
+ * Gamma(i)'s anchors, B_k^(i) (oldest first) and the chunk itself, no mask.
+ * lse: natural-log row log-sum-exp [n_heads][B_R*T] f32, or NULL.
+ * Then K, V become the newest entry of B_k (the stage-k bank keeps the last H
+ * chunks).  Order contract: chunk i must be the next chunk of stage k (0 for
+ * an empty bank), chunk i must already have run stage k-1 (k > 0), and every
+ * anchor of Gamma(i) must be published; else FF_E_ORDER / FF_E_ANCHOR_MISSING
+ * with no state change.  There is deliberately no publish-only call: the
+ * renderer has no cache-update-only forward ([S] "what it is").               */
+ff_status ff_render_attend(ff_ctx* ctx, int chunk, int stage,
+                           const void* Q, const void* K, const void* V,
+                           void* O, float* lse, void* stream);
+
+/* ff_render_attend_grouped -- n_pairs independent renderer calls in one
+ * launch of each kernel, e.g. the anti-diagonal {(t-k, k)} of the wavefront
+ * schedule ([S] "how it works": same-stage dependency; [A] abstract: a
+ * chunk's stage cache is ready for the next chunk as soon as it finishes that
+ * stage).  Each pair is validated against the state before the call, so the
+ * pairs must not depend on one another (at most one pair per stage).
+ * Results and bank contents equal n_pairs ff_render_attend calls.
+ * 1 <= n_pairs <= 8; arrays are host arrays of length n_pairs; lse[p] may be
+ * NULL and lse itself may be NULL.                                           */
+ff_status ff_render_attend_grouped(ff_ctx* ctx, int n_pairs, const int* chunks, const int* stages,
+                                   const void* const* Q, const void* const* K, const void* const* V,
+                                   void* const* O, float* const* lse, void* stream);
+
+/* ff_bank_tail -- contents of B_k: *n_out chunk ids, oldest first, written to
+ * chunk_ids[0..H-1] (host) immediately; if K_out / V_out are non-NULL their
+ * bytes ([n*B_R*T][n_heads][head_dim], the published K/V in the same order)
+ * are enqueued on the stream.  [S] "how it works", Eq. (2), Tail_H.          */
+ff_status ff_bank_tail(const ff_ctx* ctx, int stage, int* n_out, int* chunk_ids,
+                       void* K_out, void* V_out, void* stream);
+
+/* ff_gamma -- Gamma(chunk) under the context's rule: *n_out (<= 3) anchor ids,
+ * ascending, into anchor_ids[0..2].  Host only.                               */
+ff_status ff_gamma(const ff_ctx* ctx, int chunk, int* n_out, int* anchor_ids);
+
+/* ff_key_plan -- the key sources ff_render_attend(chunk, stage) would read in
+ * the current state (after the W_ctx cap).  Host only; validates the order
+ * contract exactly like ff_render_attend.                                     */
+ff_status ff_key_plan(const ff_ctx* ctx, int chunk, int stage, ff_key_sources* out);
+
+/* Next chunk id stage k expects (== number of chunks it has published). */
+ff_status ff_stage_next(const ff_ctx* ctx, int stage, int* next_chunk);
+
+/* ff_stage_bank_rewind -- undo the newest publish of stage k (retry of that
+ * chunk, or a steady-state replay).  Exact because the ring keeps H+1 slots:
+ * the chunk the undone publish evicted is still intact.  Allowed once per
+ * publish, and only if stage k+1 has not consumed that chunk; else
+ * FF_E_STATE.  Host metadata only; enqueues nothing.  Not in the pages.       */
+ff_status ff_stage_bank_rewind(ff_ctx* ctx, int stage);
+
+/* Per-kernel device timing: while enabled, each launch is bracketed by HIP
+ * events on its stream; ff_profile_read synchronises those events and returns
+ * the accumulated totals since enabling (enable also resets them).            */
+ff_status ff_profile_enable(ff_ctx* ctx, int on);
+ff_status ff_profile_read(ff_ctx* ctx, ff_kernel_times* out);
+
+/* Static description of a status code. */
+const char* ff_status_str(ff_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* FF_H_ */

@@ -1,0 +1,194 @@
+"""Side-by-side driver for GPU parity tests: HIP path (through the C ABI) and
+the CPU oracle consume the same seeded bytes and are compared call by call."""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+import oracle as orc
+import synthetic as syn
+from chunked_kv_cache_amd import ff
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}          # O max-abs gates
+LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
+RELF_TOL = {"bf16": 1e-2, "f32": 1e-5}     # relative Frobenius (diagnostic gate)
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def from_device_f64(t) -> np.ndarray:
+    import torch
+    return t.float().cpu().numpy().astype(np.float64) if t.dtype == torch.bfloat16 else \
+        t.cpu().numpy().astype(np.float64)
+
+
+@dataclass
+class Case:
+    T: int
+    nh: int
+    d: int
+    n_latents: int = 81
+    S: int = 4
+    H: int = 5
+    w_ctx: int = 21
+    dtype: str = "bf16"
+    rule: str = orc.GAMMA_BRACKET
+    seed: int = 0
+    q_scale: float = 1.0
+
+    @property
+    def cfg(self) -> orc.FFConfig:
+        return orc.FFConfig(tokens_per_latent=self.T, n_heads=self.nh, head_dim=self.d, n_latents=self.n_latents,
+                            n_stages=self.S, history=self.H, w_ctx=self.w_ctx, gamma_rule=self.rule)
+
+    def shape(self) -> ff.ff_shape:
+        return ff.make_shape(n_heads=self.nh, head_dim=self.d, tokens_per_latent=self.T, n_latents=self.n_latents,
+                             w_ctx=self.w_ctx, dtype=ff.FF_BF16 if self.dtype == "bf16" else ff.FF_F32,
+                             gamma_rule=ff.FF_GAMMA_BRACKET if self.rule == orc.GAMMA_BRACKET
+                             else ff.FF_GAMMA_CENTER_LR)
+
+
+@dataclass
+class Stats:
+    max_abs: float = 0.0
+    max_rel_fro: float = 0.0
+    max_lse: float = 0.0
+    min_control_ratio: float = math.inf
+    calls: int = 0
+    bank_checks: int = 0
+
+
+class Pair:
+    """GPU context + oracle rollout driven in lockstep."""
+
+    def __init__(self, case: Case, poison_workspace: bool = True, oracle_compute: bool = True):
+        import torch
+        self.case = case
+        self.cfg = case.cfg
+        self.banks = ff.StageBanks(case.shape(), case.S, case.H)
+        if poison_workspace:
+            # NaN everywhere the kernels must not read (spare slots, padding, partials)
+            if case.dtype == "bf16":
+                self.banks.workspace.view(torch.int16).fill_(0x7FC0)
+            else:
+                self.banks.workspace[: self.banks.ws_bytes // 4 * 4].view(torch.float32).fill_(float("nan"))
+        self.ro = orc.Rollout(self.cfg)
+        self.inputs = {}
+        self.stats = Stats()
+        self.oracle_compute = oracle_compute
+
+    @property
+    def ctx(self):
+        return self.banks.ctx
+
+    def publish_anchors(self):
+        c = self.case
+        for blk in orc.planner_blocks(self.cfg):
+            K, V = syn.anchor_kv(T=c.T, n_heads=c.nh, head_dim=c.d, anchors=blk, seed=c.seed, dtype=c.dtype)
+            ff.ff_anchor_bank_publish(self.ctx, blk[0], len(blk), to_device(K, c.dtype), to_device(V, c.dtype))
+            self.ro.publish_anchors(blk[0], syn.as_f64(K, c.dtype), syn.as_f64(V, c.dtype))
+
+    def gen(self, i, k):
+        c = self.case
+        return syn.chunk_qkv(T=c.T, n_heads=c.nh, head_dim=c.d, chunk=i, stage=k, seed=c.seed, dtype=c.dtype,
+                             q_scale=c.q_scale)
+
+    def step(self, pairs: Sequence[tuple], grouped: bool, rows: Optional[np.ndarray] = None,
+             check_bank: bool = True, control: bool = False):
+        """Run pairs [(i, k), ...] on the GPU (one grouped call or one call each), then the oracle."""
+        import torch
+        c = self.case
+        host = [self.gen(i, k) for i, k in pairs]
+        dev = [[to_device(x, c.dtype) for x in h] for h in host]
+        tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        outs = [torch.full_like(d[0], float("nan"), dtype=tdt) for d in dev]
+        lses = [torch.full((c.nh, 3 * c.T), float("nan"), dtype=torch.float32, device="cuda") for _ in dev]
+        controls = []
+        if control:
+            for (i, k), h in zip(pairs, host):
+                controls.append(self._control(i, k, h, rows))
+        if grouped:
+            ff.ff_render_attend_grouped(self.ctx, [i for i, _ in pairs], [k for _, k in pairs],
+                                        [d[0] for d in dev], [d[1] for d in dev], [d[2] for d in dev], outs, lses)
+        else:
+            for (i, k), d, o, l in zip(pairs, dev, outs, lses):
+                ff.ff_render_attend(self.ctx, i, k, d[0], d[1], d[2], o, l)
+        torch.cuda.synchronize()
+        results = []
+        for j, ((i, k), h) in enumerate(zip(pairs, host)):
+            q64, k64, v64 = (syn.as_f64(x, c.dtype) for x in h)
+            O_ref, L_ref = self.ro.render_attend(i, k, q64, k64, v64, rows=rows, compute=self.oracle_compute)
+            self.inputs[(i, k)] = (h[1], h[2])
+            if self.oracle_compute:
+                O = from_device_f64(outs[j])
+                L = lses[j].cpu().numpy().astype(np.float64)
+                if rows is not None:
+                    O, L = O[rows], L[:, rows]
+                self._compare(O, L, O_ref, L_ref, controls[j] if control else None)
+                results.append((O, O_ref))
+            if check_bank:
+                self.check_bank(k)
+        return results
+
+    def _control(self, i, k, host, rows):
+        """Negative control: the oracle with the anchor sources dropped."""
+        c = self.case
+        Kc, Vc = self.ro.gather_keys(i, k, syn.as_f64(host[1], c.dtype), syn.as_f64(host[2], c.dtype))
+        n_anchor_tok = c.T * len(orc.gamma(self.cfg, i))
+        q = syn.as_f64(host[0], c.dtype)
+        if rows is not None:
+            q = q[rows]
+        O, _ = orc.attention(q, Kc[n_anchor_tok:], Vc[n_anchor_tok:], self.cfg.scale)
+        return O
+
+    def _compare(self, O, L, O_ref, L_ref, O_ctrl):
+        dt = self.case.dtype
+        assert np.all(np.isfinite(O)), "non-finite output"
+        err = np.abs(O - O_ref).max()
+        relf = np.linalg.norm(O - O_ref) / np.linalg.norm(O_ref)
+        lerr = np.abs(L - L_ref).max()
+        st = self.stats
+        st.max_abs = max(st.max_abs, err)
+        st.max_rel_fro = max(st.max_rel_fro, relf)
+        st.max_lse = max(st.max_lse, lerr)
+        st.calls += 1
+        assert err <= TOL[dt], f"O max-abs {err:.3e} > {TOL[dt]}"
+        assert relf <= RELF_TOL[dt], f"O rel-Frobenius {relf:.3e} > {RELF_TOL[dt]}"
+        assert lerr <= LSE_TOL[dt], f"LSE max-abs {lerr:.3e} > {LSE_TOL[dt]}"
+        if O_ctrl is not None:
+            ratio = np.linalg.norm(O - O_ctrl) / max(np.linalg.norm(O - O_ref), 1e-30)
+            st.min_control_ratio = min(st.min_control_ratio, ratio)
+            assert ratio >= 10.0, f"GPU only {ratio:.1f}x closer to the oracle than to the anchor-less control"
+
+    def check_bank(self, k):
+        """B_k ids and bytes must equal the oracle's bank and the generated bits exactly."""
+        import torch
+        c = self.case
+        ids_ref, K_ref, V_ref = self.ro.bank_tail(k)
+        n = len(ids_ref)
+        tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        Ko = torch.empty((max(n, 1) * 3 * c.T, c.nh, c.d), dtype=tdt, device="cuda")
+        Vo = torch.empty_like(Ko)
+        ids = ff.ff_bank_tail(self.ctx, k, Ko, Vo)
+        assert ids == ids_ref
+        if n == 0:
+            return
+        torch.cuda.synchronize()
+        kbits = np.concatenate([self.inputs[(i, k)][0] for i in ids])
+        vbits = np.concatenate([self.inputs[(i, k)][1] for i in ids])
+        view = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) if c.dtype == "bf16" else \
+            (lambda t: t.cpu().numpy())
+        assert np.array_equal(view(Ko), kbits) and np.array_equal(view(Vo), vbits)
+        assert np.array_equal(from_device_f64(Ko), K_ref) and np.array_equal(from_device_f64(Vo), V_ref)
+        self.stats.bank_checks += 1
+
+    def close(self):
+        self.banks.close()

@@ -1,0 +1,311 @@
+"""CPU tests of the C ABI: exports, and the host bookkeeping against the oracle.
+
+libff.so is loaded and its exports are checked against include/ff.h; no
+compute call is made on it without a GPU except error paths that return
+before any device work.  The success paths (ring metadata, Tail_H ids, the
+key-source table handed to the attention kernel, error atomicity) run on
+libff_hostcheck.so: the same host source linked against a recording stub.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as orc
+from chunked_kv_cache_amd import ff
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ff.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:ff_status|size_t|void|const char\*)\s+(ff_\w+)\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    fns = header_functions()
+    for name in ("ff_anchor_bank_publish", "ff_stage_bank_create", "ff_render_attend", "ff_bank_tail"):
+        assert name in fns
+    assert sorted(ff.SYMBOLS) == fns
+
+
+@pytest.mark.parametrize("path", [ff.LIB_PATH, ff.HOSTCHECK_PATH])
+def test_library_exports_every_declared_symbol(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(ff_\w+)$", out, re.M))
+    missing = [f for f in header_functions() if f not in exported]
+    assert not missing, missing
+    lib = ff.load(path)                     # loads and binds every prototype
+    assert lib.ff_status_str(ff.FF_E_ORDER).startswith(b"order")
+
+
+def test_product_library_rejects_before_device_work():
+    """libff.so validates before touching the GPU, so these run on a CPU host."""
+    L = ff.load(ff.LIB_PATH)
+    shape = ff.make_shape(n_heads=2, head_dim=128, tokens_per_latent=16)
+    need = ff.ff_workspace_bytes(shape, 4, 5, L=L)
+    buf, addr = _aligned_buffer(need)
+    ctx = ff.ff_stage_bank_create(shape, 4, 5, addr, need, L=L)
+    try:
+        with pytest.raises(ff.FFError) as e:             # anchors of Gamma(0) missing
+            ff.ff_render_attend(ctx, 0, 0, 256, 256, 256, 256, L=L)
+        assert e.value.status == ff.FF_E_ANCHOR_MISSING
+        with pytest.raises(ff.FFError) as e:
+            ff.ff_render_attend(ctx, 1, 0, 256, 256, 256, 256, L=L)
+        assert e.value.status == ff.FF_E_ORDER
+    finally:
+        ff.ff_destroy(ctx, L=L)
+
+
+# --------------------------------------------------------------------------
+# Host-check library (recording stub instead of kernels)
+# --------------------------------------------------------------------------
+def _aligned_buffer(nbytes):
+    raw = np.zeros(nbytes + 512, dtype=np.uint8)
+    addr = raw.ctypes.data
+    addr = (addr + 255) // 256 * 256
+    return raw, addr
+
+
+class HostCtx:
+    def __init__(self, cfg: orc.FFConfig, w_ctx=None, dtype=ff.FF_BF16):
+        self.L = ff.load(ff.HOSTCHECK_PATH)
+        self.cfg = cfg
+        rule = ff.FF_GAMMA_BRACKET if cfg.gamma_rule == orc.GAMMA_BRACKET else ff.FF_GAMMA_CENTER_LR
+        self.shape = ff.make_shape(n_heads=cfg.n_heads, head_dim=cfg.head_dim,
+                                   tokens_per_latent=cfg.tokens_per_latent, chunk_latents=cfg.chunk_latents,
+                                   anchor_stride=cfg.anchor_stride, n_latents=cfg.n_latents,
+                                   w_ctx=cfg.w_ctx if w_ctx is None else w_ctx, dtype=dtype, gamma_rule=rule)
+        self.need = ff.ff_workspace_bytes(self.shape, cfg.n_stages, cfg.history, L=self.L)
+        self.raw, self.ws = _aligned_buffer(self.need)
+        self.ctx = ff.ff_stage_bank_create(self.shape, cfg.n_stages, cfg.history, self.ws, self.need, L=self.L)
+
+    def counts(self):
+        c = [ctypes.c_int() for _ in range(4)]
+        self.L.ffstub_counts(*[ctypes.byref(x) for x in c])
+        return [x.value for x in c]
+
+    def last_segments(self, p=0):
+        off = (ctypes.c_longlong * 16)()
+        n = (ctypes.c_int * 16)()
+        lk, ns = ctypes.c_int(), ctypes.c_int()
+        f = self.L.ffstub_last_segments
+        f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                      ctypes.c_void_p]
+        k = f(p, self.ws, off, n, ctypes.byref(lk), ctypes.byref(ns))
+        return list(off[:k]), list(n[:k]), lk.value, ns.value
+
+    def last_copy_block(self, j):
+        f = self.L.ffstub_last_copy_block
+        f.restype = ctypes.c_longlong
+        f.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        return f(j, self.ws)
+
+    def close(self):
+        ff.ff_destroy(self.ctx, L=self.L)
+
+
+def _layout(cfg):
+    esz = 2
+    T, nh, d = cfg.tokens_per_latent, cfg.n_heads, cfg.head_dim
+    al = lambda x: (x + 255) // 256 * 256
+    anchor_block = al(2 * nh * T * d * esz)
+    slot_block = al(2 * nh * 3 * T * d * esz)
+    slot_off = orc.n_anchors(cfg) * anchor_block
+    return anchor_block, slot_block, slot_off
+
+
+FAKE = 1 << 20      # 16-byte aligned stand-in device addresses; the stub never reads them
+
+
+def _publish_anchors(hc):
+    for blk in orc.planner_blocks(hc.cfg):
+        ff.ff_anchor_bank_publish(hc.ctx, blk[0], len(blk), FAKE, FAKE, L=hc.L)
+
+
+@pytest.mark.parametrize("rule", [orc.GAMMA_BRACKET, orc.GAMMA_CENTER_LR])
+@pytest.mark.parametrize("L", [81, 261])
+def test_gamma_matches_oracle(rule, L):
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=64, n_latents=L, gamma_rule=rule)
+    hc = HostCtx(cfg)
+    try:
+        for i in range(orc.n_chunks(cfg)):
+            assert ff.ff_gamma(hc.ctx, i, L=hc.L) == orc.gamma(cfg, i)
+    finally:
+        hc.close()
+
+
+@pytest.mark.parametrize("rule", [orc.GAMMA_BRACKET, orc.GAMMA_CENTER_LR])
+def test_rollout_bookkeeping_matches_oracle(rule):
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=3, head_dim=128, gamma_rule=rule)
+    hc = HostCtx(cfg)
+    ro = orc.Rollout(cfg)
+    anchor_block, slot_block, slot_off = _layout(cfg)
+    z = np.zeros((48, 3, 128))
+    c0 = hc.counts()
+    try:
+        _publish_anchors(hc)
+        for blk in orc.planner_blocks(cfg):
+            ro.publish_anchors(blk[0], np.zeros((16 * len(blk), 3, 128)), np.zeros((16 * len(blk), 3, 128)))
+        for diag in orc.schedule(cfg):
+            for i, k in diag:
+                plan = ff.ff_key_plan(hc.ctx, i, k, L=hc.L)
+                src = ro.key_sources(i, k)
+                kinds = {ff.FF_SRC_ANCHOR: "anchor", ff.FF_SRC_HISTORY: "history", ff.FF_SRC_OWN: "own"}
+                got = [(kinds[plan.kind[j]], plan.id[j]) for j in range(plan.n_sources)]
+                assert got == src
+                ntok = [16 if s == "anchor" else 48 for s, _ in src]
+                assert list(plan.n_tokens[:plan.n_sources]) == ntok
+                assert plan.key_tokens == sum(ntok)
+                ff.ff_render_attend(hc.ctx, i, k, FAKE, FAKE, FAKE, FAKE, L=hc.L)
+                ro.render_attend(i, k, None, z, z, compute=False)
+                # the key table handed to the kernel points at the right blocks
+                offs, ntoks, lk, _ = hc.last_segments()
+                assert ntoks == ntok and lk == sum(ntok)
+                for (s, idx), off in zip(src, offs):
+                    if s == "anchor":
+                        assert off == idx * anchor_block
+                    else:
+                        assert off == slot_off + (k * 6 + idx % 6) * slot_block
+                # the publish went to slot i mod (H+1) of stage k
+                assert hc.last_copy_block(0) == slot_off + (k * 6 + i % 6) * slot_block
+                assert ff.ff_bank_tail(hc.ctx, k, L=hc.L) == ro.bank_tail(k)[0]
+                assert ff.ff_stage_next(hc.ctx, k, L=hc.L) == i + 1
+        assert [a - b for a, b in zip(hc.counts(), c0)][:3] == [108, 108, 3]
+    finally:
+        hc.close()
+
+
+def test_grouped_calls_match_single_calls_bookkeeping():
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=128, n_latents=261)
+    hc = HostCtx(cfg)
+    c0 = hc.counts()
+    try:
+        _publish_anchors(hc)
+        for diag in orc.schedule(cfg):
+            chunks = [i for i, _ in diag]
+            stages = [k for _, k in diag]
+            n = len(diag)
+            ff.ff_render_attend_grouped(hc.ctx, chunks, stages, [FAKE] * n, [FAKE] * n, [FAKE] * n,
+                                        [FAKE] * n, L=hc.L)
+        for k in range(4):
+            assert ff.ff_bank_tail(hc.ctx, k, L=hc.L) == list(range(82, 87))
+        assert hc.counts()[0] - c0[0] == 90
+    finally:
+        hc.close()
+
+
+def test_error_paths_leave_state_unchanged():
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=128)
+    hc = HostCtx(cfg)
+    L = hc.L
+    F = FAKE
+
+    def status(fn, *a):
+        try:
+            fn(*a, L=L)
+            return ff.FF_OK
+        except ff.FFError as e:
+            return e.status
+
+    try:
+        assert status(ff.ff_render_attend, hc.ctx, 0, 0, F, F, F, F) == ff.FF_E_ANCHOR_MISSING
+        ff.ff_anchor_bank_publish(hc.ctx, 0, 3, F, F, L=L)
+        assert status(ff.ff_anchor_bank_publish, hc.ctx, 2, 1, F, F) == ff.FF_E_ANCHOR_EXISTS
+        assert status(ff.ff_anchor_bank_publish, hc.ctx, 8, 2, F, F) == ff.FF_E_RANGE
+        assert status(ff.ff_anchor_bank_publish, hc.ctx, 3, 1, F + 8, F) == ff.FF_E_INVAL
+        before = hc.counts()
+        assert status(ff.ff_render_attend, hc.ctx, 1, 0, F, F, F, F) == ff.FF_E_ORDER      # skips chunk 0
+        assert status(ff.ff_render_attend, hc.ctx, 0, 1, F, F, F, F) == ff.FF_E_ORDER      # stage 0 not run
+        assert status(ff.ff_render_attend, hc.ctx, 0, 4, F, F, F, F) == ff.FF_E_RANGE
+        assert status(ff.ff_render_attend, hc.ctx, 27, 0, F, F, F, F) == ff.FF_E_RANGE
+        assert status(ff.ff_render_attend, hc.ctx, 0, 0, 0, F, F, F) == ff.FF_E_INVAL
+        assert status(ff.ff_render_attend, hc.ctx, 0, 0, F, F, F, F + 4) == ff.FF_E_INVAL
+        assert status(ff.ff_render_attend, hc.ctx, 0, 0, F, F, F, F, F + 2) == ff.FF_E_INVAL   # lse
+        assert hc.counts() == before and ff.ff_stage_next(hc.ctx, 0, L=L) == 0
+        for i in range(3):
+            ff.ff_render_attend(hc.ctx, i, 0, F, F, F, F, L=L)
+        # grouped: a pair that depends on another pair of the same call is refused atomically
+        assert status(ff.ff_render_attend_grouped, hc.ctx, [0, 0], [1, 2], [F] * 2, [F] * 2, [F] * 2,
+                      [F] * 2) == ff.FF_E_ORDER
+        assert status(ff.ff_render_attend_grouped, hc.ctx, [0, 1], [1, 1], [F] * 2, [F] * 2, [F] * 2,
+                      [F] * 2) == ff.FF_E_ORDER
+        assert ff.ff_stage_next(hc.ctx, 1, L=L) == 0
+        # rewind: once per publish, and not under a later stage that consumed the chunk
+        ff.ff_render_attend(hc.ctx, 0, 1, F, F, F, F, L=L)
+        assert status(ff.ff_stage_bank_rewind, hc.ctx, 0) == ff.FF_OK            # chunk 2 of stage 0
+        assert ff.ff_stage_next(hc.ctx, 0, L=L) == 2
+        assert ff.ff_bank_tail(hc.ctx, 0, L=L) == [0, 1]
+        assert status(ff.ff_stage_bank_rewind, hc.ctx, 0) == ff.FF_E_STATE
+        ff.ff_render_attend(hc.ctx, 2, 0, F, F, F, F, L=L)
+        assert status(ff.ff_stage_bank_rewind, hc.ctx, 1) == ff.FF_OK
+        assert status(ff.ff_stage_bank_rewind, hc.ctx, 2) == ff.FF_E_STATE
+    finally:
+        hc.close()
+
+
+def test_rewind_after_stage_consumed_is_refused():
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=128)
+    hc = HostCtx(cfg)
+    try:
+        _publish_anchors(hc)
+        ff.ff_render_attend(hc.ctx, 0, 0, FAKE, FAKE, FAKE, FAKE, L=hc.L)
+        ff.ff_render_attend(hc.ctx, 0, 1, FAKE, FAKE, FAKE, FAKE, L=hc.L)
+        with pytest.raises(ff.FFError) as e:
+            ff.ff_stage_bank_rewind(hc.ctx, 0, L=hc.L)
+        assert e.value.status == ff.FF_E_STATE
+        ff.ff_stage_bank_rewind(hc.ctx, 1, L=hc.L)
+        ff.ff_stage_bank_rewind(hc.ctx, 0, L=hc.L)
+        assert [ff.ff_stage_next(hc.ctx, k, L=hc.L) for k in range(4)] == [0, 0, 0, 0]
+    finally:
+        hc.close()
+
+
+def test_w_ctx_cap_matches_oracle():
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=64, w_ctx=11, n_stages=1)
+    hc = HostCtx(cfg)
+    ro = orc.Rollout(cfg)
+    z = np.zeros((48, 2, 64))
+    try:
+        _publish_anchors(hc)
+        for blk in orc.planner_blocks(cfg):
+            ro.publish_anchors(blk[0], np.zeros((16 * len(blk), 2, 64)), np.zeros((16 * len(blk), 2, 64)))
+        for i in range(orc.n_chunks(cfg)):
+            plan = ff.ff_key_plan(hc.ctx, i, 0, L=hc.L)
+            assert plan.key_latents <= 11 or plan.n_sources == len(orc.gamma(cfg, i)) + 1
+            assert [plan.id[j] for j in range(plan.n_sources)] == [x for _, x in ro.key_sources(i, 0)]
+            ff.ff_render_attend(hc.ctx, i, 0, FAKE, FAKE, FAKE, FAKE, L=hc.L)
+            ro.render_attend(i, 0, None, z, z, compute=False)
+    finally:
+        hc.close()
+
+
+@pytest.mark.parametrize("bad", [dict(head_dim=96), dict(tokens_per_latent=12), dict(tokens_per_latent=4),
+                                 dict(chunk_latents=11), dict(n_latents=82), dict(dtype=7), dict(gamma_rule=5),
+                                 dict(n_heads=0)])
+def test_unsupported_shapes_are_rejected(bad):
+    L = ff.load(ff.HOSTCHECK_PATH)
+    kw = dict(n_heads=2, head_dim=128, tokens_per_latent=16)
+    kw.update(bad)
+    shape = ff.make_shape(**kw)
+    assert ff.ff_workspace_bytes(shape, 4, 5, L=L) == 0
+    with pytest.raises(ff.FFError) as e:
+        ff.ff_stage_bank_create(shape, 4, 5, 256, 1 << 30, L=L)
+    assert e.value.status == ff.FF_E_INVAL
+
+
+def test_history_and_workspace_limits():
+    L = ff.load(ff.HOSTCHECK_PATH)
+    shape = ff.make_shape(n_heads=2, head_dim=128, tokens_per_latent=16)
+    assert ff.ff_workspace_bytes(shape, 4, 9, L=L) == 0
+    need = ff.ff_workspace_bytes(shape, 4, 5, L=L)
+    with pytest.raises(ff.FFError) as e:
+        ff.ff_stage_bank_create(shape, 4, 5, 256, need - 1, L=L)
+    assert e.value.status == ff.FF_E_NOSPACE
+    with pytest.raises(ff.FFError) as e:
+        ff.ff_stage_bank_create(shape, 4, 5, 256 + 16, need, L=L)     # workspace not 256-aligned
+    assert e.value.status == ff.FF_E_INVAL
