@@ -1,0 +1,223 @@
+"""Benchmark of the renderer hot path on one MI355X.
+
+A step is one ff_render_attend call at steady state: publish of the chunk's
+K/V into its stage bank (Tail_H) plus segmented attention over the Gamma(i)
+anchors, the H = 5 history chunks and the chunk itself, host bookkeeping
+included.  The default workload is the 480p-shaped step: 12 heads, head_dim
+128, T = 1560 tokens per latent, chunk 5 (Gamma = 2 anchors + 5 history
+chunks + own = 20 latents: 4680 queries x 31200 keys).  Steps rotate over the
+S = 4 stage banks (4 distinct key sets, 0.77 GB, more than the 256 MB
+last-level cache); before each round the four banks are rewound by one chunk
+(ff_stage_bank_rewind) so the same steady-state call repeats.
+
+Prints one JSON line.  `value` = attention TFLOP/s of the whole step
+(algorithmic 4*Lq*Lk*d*nh FLOPs / wall time per step).  `roofline` = the
+attention kernel alone, from HIP events on the launch stream.  `cpu_baseline`
+= the float64 CPU oracle on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+
+WORKLOADS = {
+    # name: (T, nh, chunk, n_latents, S, description)
+    "step480": (1560, 12, 5, 81, 4, "480p renderer step: chunk 5, 4680 queries x 31200 keys "
+                                     "(2 anchors + 5 history chunks + own 3 latents), 12 heads x 128"),
+    "step480_21": (1560, 12, 13, 81, 4, "480p renderer step at the 21-latent cap: chunk 13, 4680 queries x "
+                                         "32760 keys (3 anchors + 5 history + own), 12 heads x 128"),
+    "step720": (3600, 40, 5, 81, 1, "720p renderer step: chunk 5, 10800 queries x 72000 keys "
+                                    "(2 anchors + 5 history + own), 40 heads x 128"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="step480", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the CPU oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the stage-sharded multi-GPU path is a design, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic as syn
+    from chunked_kv_cache_amd import ff
+
+    T, nh, chunk, n_latents, S, desc = WORKLOADS[args.workload]
+    d, H = 128, 5
+    torch.cuda.set_device(0)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16).cuda()
+    shape = ff.make_shape(n_heads=nh, head_dim=d, tokens_per_latent=T, n_latents=n_latents)
+    banks = ff.StageBanks(shape, S, H)
+    ctx = banks.ctx
+    Lq = 3 * T
+
+    t0 = time.time()
+    n_anchor = (n_latents + 9) // 10
+    for a0 in range(0, n_anchor, 3):
+        blk = list(range(a0, min(a0 + 3, n_anchor)))
+        K, V = syn.anchor_kv(T=T, n_heads=nh, head_dim=d, anchors=blk)
+        ff.ff_anchor_bank_publish(ctx, blk[0], len(blk), dev(K), dev(V))
+    # fill every stage bank with chunks 0..chunk in wavefront order
+    step_inputs = {}
+    scratch_o = torch.empty((Lq, nh, d), dtype=torch.bfloat16, device="cuda")
+    for t in range(chunk + S):
+        for k in range(S):
+            i = t - k
+            if 0 <= i <= chunk:
+                q, kk, vv = syn.chunk_qkv(T=T, n_heads=nh, head_dim=d, chunk=i, stage=k)
+                qd, kd, vd = dev(q), dev(kk), dev(vv)
+                if i == chunk:
+                    step_inputs[k] = (qd, kd, vd, q, kk, vv)
+                ff.ff_render_attend(ctx, i, k, qd, kd, vd, scratch_o)
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s")
+
+    outs = [torch.empty((Lq, nh, d), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    lses = [torch.empty((nh, Lq), dtype=torch.float32, device="cuda") for _ in range(S)]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def rewind_all():
+        for k in reversed(range(S)):
+            ff.ff_stage_bank_rewind(ctx, k)
+
+    def one_step(j):
+        k = j % S
+        if k == 0:
+            rewind_all()
+        qd, kd, vd = step_inputs[k][:3]
+        ff.ff_render_attend(ctx, chunk, k, qd, kd, vd, outs[k], lses[k], stream=stream)
+
+    # the stage banks currently hold chunk `chunk` published once; start a round
+    key_plan = None
+    rewind_all()
+    for k in range(S):
+        if key_plan is None:
+            key_plan = ff.ff_key_plan(ctx, chunk, k)
+        qd, kd, vd = step_inputs[k][:3]
+        ff.ff_render_attend(ctx, chunk, k, qd, kd, vd, outs[k], lses[k], stream=stream)
+    Lk = key_plan.key_tokens
+    flops = 4.0 * Lq * Lk * d * nh
+    pub_bytes = 2 * 2 * Lq * nh * d * 2          # K and V, read + write, bf16
+
+    steps_done = S
+    for _ in range(args.warmup):
+        one_step(steps_done)
+        steps_done += 1
+    # align the timed region to the start of a round
+    while steps_done % S:
+        one_step(steps_done)
+        steps_done += 1
+    torch.cuda.synchronize()
+
+    ff.ff_profile_enable(ctx, True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for j in range(args.steps):
+        one_step(steps_done + j)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    prof = ff.ff_profile_read(ctx)
+    ff.ff_profile_enable(ctx, False)
+
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = flops * args.steps / wall / 1e12
+    attn_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
+    merge_ms = prof["merge_ms"] / prof["merge_launches"] if prof["merge_launches"] else 0.0
+    pub_ms = prof["publish_ms"] / max(prof["publish_launches"], 1)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    pub_gbps = pub_bytes / (pub_ms * 1e-3) / 1e9
+    log(f"attention kernel {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s), merge {merge_ms:.3f} ms, "
+        f"publish {pub_ms * 1e3:.1f} us ({pub_gbps:.0f} GB/s), step {ms_per_step:.3f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(ctx, step_inputs[0][3:], chunk, T, nh, d, args.cpu_heads, n_latents)
+
+    out = {
+        "metric": "renderer chunk-attention TFLOP/s (% bf16 MFMA peak) + chunk-steps/s; publish GB/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, shapes of the 480p/720p renderer)",
+        "config": {"workload": desc, "queries": Lq, "keys": Lk, "heads": nh, "head_dim": d,
+                   "tokens_per_latent": T, "chunk": chunk, "stage_banks": S, "history": H,
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "chunk_steps_per_s": round(args.steps / wall, 2),
+        "attention_kernel_ms": round(attn_ms, 4),
+        "merge_kernel_ms": round(merge_ms, 4),
+        "publish_kernel_us": round(pub_ms * 1e3, 2),
+        "publish_gbps": round(pub_gbps, 1),
+        "publish_pct_hbm": round(100 * pub_gbps / PEAK_HBM_GBPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    banks.close()
+
+
+def cpu_baseline(ctx, host_qkv, chunk, T, nh, d, n_heads_sample, n_latents):
+    """The float64 oracle's attention on a bounded sample of the same step:
+    all queries of the first `n_heads_sample` heads against the full key set."""
+    import numpy as np
+    import oracle as orc
+    import synthetic as syn
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                      default=len(os.sched_getaffinity(0)))
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=nh, head_dim=d, n_latents=n_latents, n_stages=1)
+    ro = orc.Rollout(cfg)
+    hs = slice(0, n_heads_sample)
+    for a in orc.gamma(cfg, chunk):
+        K, V = syn.anchor_kv(T=T, n_heads=nh, head_dim=d, anchors=[a])
+        ro.anchors[a] = (syn.as_f64(K, "bf16")[:, hs], syn.as_f64(V, "bf16")[:, hs])
+    for i in range(max(0, chunk - cfg.history), chunk):
+        _, kk, vv = syn.chunk_qkv(T=T, n_heads=nh, head_dim=d, chunk=i, stage=0)
+        ro.banks[0].append((i, syn.as_f64(kk, "bf16")[:, hs], syn.as_f64(vv, "bf16")[:, hs]))
+    ro.next_chunk[0] = chunk
+    q, kk, vv = (syn.as_f64(x, "bf16")[:, hs] for x in host_qkv)
+    Kc, Vc = ro.gather_keys(chunk, 0, kk, vv)
+    t0 = time.perf_counter()
+    orc.attention(q, Kc, Vc, cfg.scale)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * q.shape[0] * Kc.shape[0] * d * n_heads_sample
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle attention of chunk {chunk}, {n_heads_sample} of {nh} heads, all "
+                      f"{q.shape[0]} queries x {Kc.shape[0]} keys ({flops / 1e9:.0f} GFLOP in {dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

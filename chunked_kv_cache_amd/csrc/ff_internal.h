@@ -22,10 +22,13 @@ constexpr int kMaxSplit = 4;       // key-range splits per work item
 // One key source as the attention kernel sees it.  `base` points at the
 // source's block in the workspace: K head-major [nh][n][d] followed directly by
 // V transposed [nh][d][n] (both in the context dtype).
+// Every source covers ceil(n/64) whole 64-key tiles of the call's tile index
+// space, so no tile straddles two sources; the last tile of a source is
+// masked past n.
 struct SegTable {
   const void* base[kMaxSeg];
   int32_t n[kMaxSeg];              // tokens of the source (multiple of 8)
-  int32_t start[kMaxSeg + 1];      // prefix sums; start[nseg] = L_k
+  int32_t tile_start[kMaxSeg + 1]; // prefix sums of ceil(n/64); [nseg] = tiles
   int32_t nseg;
 };
 
@@ -36,6 +39,7 @@ struct PairLaunch {
   float* part;                     // split-K partials of this pair (or null)
   SegTable seg;
   int32_t lk;                      // key tokens
+  int32_t ntiles;                  // 64-key tiles (sources padded to whole tiles)
   int32_t n_split;
   int32_t tiles_per_split;
   int32_t item_base;               // first work item of this pair

@@ -38,18 +38,11 @@ constexpr float kRescaleTau = 8.0f;
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Index of the key source holding virtual key v (v < L_k).
-__device__ __forceinline__ int seg_of(const SegTable& t, int v) {
-  int s = 0;
-  while (s + 1 < t.nseg && v >= t.start[s + 1]) ++s;
-  return s;
-}
-
 // --------------------------------------------------------------------------
 // Segmented attention, bf16 in, fp32 accumulate.
 //
-// Work item = (pair, head, key split, 128-query tile); 4 waves x 32 queries.
-// Per 64-key tile:
+// Work item = (pair, head, key split, 128-query tile); 4 waves x 32 queries;
+// 2 work items per CU.  Per 64-key tile:
 //   S^T[key][q] = sum_d K[key][d] Q[q][d]     (A = K rows from LDS, B = Q regs)
 //   p = 2^(s*scale*log2e - m)                 (per query = per lane column)
 //   O^T[d][q] += sum_key V^T[d][key] P^T[key][q]  (A = V^T from LDS, B = P regs)
@@ -59,77 +52,34 @@ __device__ __forceinline__ int seg_of(const SegTable& t, int v) {
 // that accumulator registers 8*j..8*j+7 of lane l are keys 16*j + 8*(l/32) +
 // 0..7: P leaves the first MFMA already in B-operand order for the second,
 // and V^T rows are read as one contiguous 16-byte run per lane.
+//
+// K/V tiles go global -> LDS directly (global_load_lds_dwordx4, 1 KB per wave
+// instruction, lane i -> LDS bytes 16i..16i+15), double-buffered in two LDS
+// arrays.  The LDS layouts are XOR-swizzled for conflict-free 16-byte reads;
+// the swizzle is applied by choosing which global chunk each lane fetches.
 // --------------------------------------------------------------------------
 template <int D>
 struct TileCfg {
   static constexpr int kKBytes = kBlockN * D * 2;     // K tile [64][D]
   static constexpr int kVBytes = D * kBlockN * 2;     // V^T tile [D][64]
   static constexpr int kBufBytes = kKBytes + kVBytes;
-  static constexpr int kKLoads = kBlockN * (D / 8) / 256;   // 16-byte loads per thread
-  static constexpr int kVLoads = D * 8 / 256;
+  static constexpr int kKBlocks = kKBytes / 1024 / 4; // 1 KB DMA blocks per wave
+  static constexpr int kVBlocks = kVBytes / 1024 / 4;
+  static constexpr int kRowsPerKBlock = 1024 / (2 * D);
+  static constexpr int kChunksPerRow = D / 8;
 };
 
 __device__ __forceinline__ int krow_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
 
-template <int D>
-__device__ __forceinline__ void load_tile(const PairLaunch& P, int h, int nh, int v0, int tid,
-                                          u32x4 (&kr)[TileCfg<D>::kKLoads], u32x4 (&vr)[TileCfg<D>::kVLoads]) {
-  const SegTable& t = P.seg;
-  const int lk = P.lk;
-  // Tiles that lie inside one source (all but a handful) take the uniform path.
-  const int s0 = seg_of(t, v0);
-  const int s_end = t.start[s0 + 1];
-  const bool uniform = (v0 + kBlockN <= s_end) || (s_end == lk);
-  const int r0 = tid >> 3, c0 = tid & 7;
-#pragma unroll
-  for (int i = 0; i < TileCfg<D>::kKLoads; ++i) {
-    const int r = r0 + 32 * (i & 1), c = c0 + 8 * (i >> 1);
-    const int v = v0 + r;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (v < lk) {
-      const int s = uniform ? s0 : seg_of(t, v);
-      const int n = t.n[s];
-      const __bf16* kb = static_cast<const __bf16*>(t.base[s]);
-      val = ld16(kb + (int64_t(h) * n + (v - t.start[s])) * D + 8 * c);
-    }
-    kr[i] = val;
-  }
-  {
-    const int v = v0 + 8 * c0;
-    int s = s0, n = 0, off = 0;
-    const __bf16* vb = nullptr;
-    if (v < lk) {
-      s = uniform ? s0 : seg_of(t, v);
-      n = t.n[s];
-      off = v - t.start[s];
-      vb = static_cast<const __bf16*>(t.base[s]) + int64_t(nh) * n * D;
-    }
-#pragma unroll
-    for (int i = 0; i < TileCfg<D>::kVLoads; ++i) {
-      const int dd = r0 + 32 * i;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (v < lk) val = ld16(vb + (int64_t(h) * D + dd) * n + off);
-      vr[i] = val;
-    }
-  }
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void glb_void;
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds((glb_void*)(g), (lds_void*)(l), 16, 0, 0);
 }
 
-template <int D>
-__device__ __forceinline__ void store_tile(uint8_t* buf, int tid, const u32x4 (&kr)[TileCfg<D>::kKLoads],
-                                           const u32x4 (&vr)[TileCfg<D>::kVLoads]) {
-  const int r0 = tid >> 3, c0 = tid & 7;
-#pragma unroll
-  for (int i = 0; i < TileCfg<D>::kKLoads; ++i) {
-    const int r = r0 + 32 * (i & 1), c = c0 + 8 * (i >> 1);
-    st16(buf + r * (D * 2) + ((c ^ krow_swz(r)) << 4), kr[i]);
-  }
-  uint8_t* vbuf = buf + TileCfg<D>::kKBytes;
-#pragma unroll
-  for (int i = 0; i < TileCfg<D>::kVLoads; ++i) {
-    const int dd = r0 + 32 * i;
-    st16(vbuf + dd * (kBlockN * 2) + ((c0 ^ (dd & 7)) << 4), vr[i]);
-  }
-}
+// Wait until this wave's outstanding global->LDS copies have landed.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -139,9 +89,137 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
+// Key-source cursor of one wave (all fields wave-uniform).
 template <int D>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnLaunch a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TileCfg<D>::kBufBytes];
+struct SrcCursor {
+  const __bf16* k;      // K rows of this head, key 0 of the source
+  const __bf16* v;      // V^T of this head, [D][n]
+  int n, t0, t1, s;
+};
+
+template <int D>
+__device__ __forceinline__ void cursor_set(SrcCursor<D>& c, const SegTable& t, int s, int h, int nh) {
+  c.s = s;
+  c.n = t.n[s];
+  c.t0 = t.tile_start[s];
+  c.t1 = t.tile_start[s + 1];
+  const __bf16* base = static_cast<const __bf16*>(t.base[s]);
+  c.k = base + int64_t(h) * c.n * D;
+  c.v = base + int64_t(nh) * c.n * D + int64_t(h) * D * c.n;
+}
+
+// Issue the copies of tile t (inside the cursor's source) into buf.
+// Returns the number of valid keys of the tile (64 except a source's last).
+template <int D>
+__device__ __forceinline__ int issue_tile(const SrcCursor<D>& c, int t, uint8_t* buf, int w, int lane) {
+  constexpr int CPR = TileCfg<D>::kChunksPerRow;
+  const int o = (t - c.t0) * kBlockN;
+  const int valid = min(kBlockN, c.n - o);
+  const __bf16* kt = c.k + int64_t(o) * D;
+#pragma unroll
+  for (int j = 0; j < TileCfg<D>::kKBlocks; ++j) {
+    const int b = w * TileCfg<D>::kKBlocks + j;
+    int r = b * TileCfg<D>::kRowsPerKBlock + lane / CPR;
+    const int ch = (lane % CPR) ^ krow_swz(r);
+    r = r < valid ? r : 0;                           // rows past the source: any valid row
+    dma16(kt + r * D + ch * 8, buf + b * 1024);
+  }
+  const __bf16* vt = c.v + o;
+  uint8_t* vbuf = buf + TileCfg<D>::kKBytes;
+#pragma unroll
+  for (int j = 0; j < TileCfg<D>::kVBlocks; ++j) {
+    const int b = w * TileCfg<D>::kVBlocks + j;
+    const int dd = b * 8 + lane / 8;
+    int ch = (lane & 7) ^ (dd & 7);
+    ch = ch * 8 < valid ? ch : 0;
+    dma16(vt + int64_t(dd) * c.n + ch * 8, vbuf + b * 1024);
+  }
+  return valid;
+}
+
+template <int D>
+struct Acc {
+  f32x16 o[D / 32];
+  float m, l;
+};
+
+// One 64-key tile from LDS: S^T, softmax update, O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void compute_tile(const uint8_t* buf, int valid, const bf16x8 (&qreg)[D / 16],
+                                             Acc<D>& acc, float c, int l32, int hl, int prow) {
+  constexpr int KS = D / 16, DB = D / 32;
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int row = 32 * kb + prow;
+    const uint8_t* kbase = buf + row * (D * 2);
+    const int sw = krow_swz(row);
+    const f32x16 zero = {};
+    s[kb] = zero;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch = 2 * ks + hl;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(kbase + ((ch ^ sw) << 4)));
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], s[kb], 0, 0, 0);
+    }
+  }
+  if (valid < kBlockN) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
+        if (key >= valid) s[kb][r] = -INFINITY;
+      }
+  }
+  float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mx2 = mx * c;
+  if (__builtin_expect(__ballot(mx2 > acc.m + kRescaleTau) != 0, 0)) {
+    const float m_new = fmaxf(acc.m, mx2);
+    const float alpha = __builtin_amdgcn_exp2f(acc.m - m_new);
+    acc.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc.o[db][r] *= alpha;
+    acc.m = m_new;
+  }
+  const float nm = -acc.m;
+  bf16x8 pb[2][2];
+  float lsum = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * j + e], c, nm));
+        lsum += pv;
+        pb[kb][j][e] = (__bf16)pv;
+      }
+  acc.l += lsum;
+  const uint8_t* vbase = buf + TileCfg<D>::kKBytes;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ch = 4 * kb + 2 * j + hl;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int dd = 32 * db + l32;
+        const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ (dd & 7)) << 4)));
+        acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][j], acc.o[db], 0, 0, 0);
+      }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnLaunch a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TileCfg<D>::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TileCfg<D>::kBufBytes];
   constexpr int KS = D / 16;       // MFMA k-steps over head_dim
   constexpr int DB = D / 32;       // 32-row blocks of O^T
 
@@ -157,127 +235,65 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnLaunch a) {
   const int split = local / nh;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
   const int q = qt * kBlockM + w * 32 + l32;
   const bool q_ok = q < lq;
 
   // Q^T as the B operand: lane holds Q[q][16*ks + 8*hl .. +7].
   bf16x8 qreg[KS];
   {
-    const __bf16* qp = static_cast<const __bf16*>(P.q) + (int64_t(q) * nh + h) * D + 8 * hl;
+    const __bf16* qp = static_cast<const __bf16*>(P.q) + (int64_t(q_ok ? q : 0) * nh + h) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (q_ok) v = ld16(qp + 16 * ks);
+      u32x4 v = ld16(qp + 16 * ks);
+      if (!q_ok) v = u32x4{0u, 0u, 0u, 0u};
       qreg[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  const int ntiles = (P.lk + kBlockN - 1) / kBlockN;
   const int t_begin = split * P.tiles_per_split;
-  const int t_end = min(ntiles, t_begin + P.tiles_per_split);
+  const int t_end = min(P.ntiles, t_begin + P.tiles_per_split);
   const float c = a.scale * kLog2e;
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-
   // Row of the K tile this lane feeds as A operand (bits 2 and 3 swapped).
   const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
 
-  u32x4 kr[TileCfg<D>::kKLoads], vr[TileCfg<D>::kVLoads];
-  load_tile<D>(P, h, nh, t_begin * kBlockN, tid, kr, vr);
-  store_tile<D>(lds, tid, kr, vr);
+  Acc<D> acc;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc.o[db][r] = 0.f;
+  acc.m = -INFINITY;
+  acc.l = 0.f;
+
+  SrcCursor<D> cur;
+  {
+    int s = 0;
+    while (s + 1 < P.seg.nseg && t_begin >= P.seg.tile_start[s + 1]) ++s;
+    cursor_set<D>(cur, P.seg, s, h, nh);
+  }
+  auto issue = [&](int t, uint8_t* buf) -> int {
+    if (t >= cur.t1) cursor_set<D>(cur, P.seg, cur.s + 1, h, nh);
+    return issue_tile<D>(cur, t, buf, w, lane);
+  };
+
+  int valid0 = issue(t_begin, lds0), valid1 = 0;
+  wait_dma();
   __syncthreads();
-
-  for (int t = t_begin; t < t_end; ++t) {
-    uint8_t* buf = lds + ((t - t_begin) & 1) * TileCfg<D>::kBufBytes;
-    const bool more = t + 1 < t_end;
-    if (more) load_tile<D>(P, h, nh, (t + 1) * kBlockN, tid, kr, vr);
-
-    // ---- S^T = K Q^T for two 32-key blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-      const int row = 32 * kb + prow;
-      const uint8_t* kbase = buf + row * (D * 2);
-      const int sw = krow_swz(row);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch = 2 * ks + hl;
-        const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(kbase + ((ch ^ sw) << 4)));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], s[kb], 0, 0, 0);
-      }
-    }
-
-    // ---- mask keys past L_k (last tile only)
-    const int v0 = t * kBlockN;
-    if (v0 + kBlockN > P.lk) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = v0 + 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-          if (key >= P.lk) s[kb][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax (base 2), lazy rescale
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mx2 = mx * c;
-    if (__ballot(mx2 > m_run + kRescaleTau)) {
-      const float m_new = fmaxf(m_run, mx2);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      m_run = m_new;
-    }
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * j + e], c, -m_run));
-          l_run += pv;
-          pb[kb][j][e] = (__bf16)pv;
-        }
-
-    // ---- O^T += V^T P^T
-    const uint8_t* vbase = buf + TileCfg<D>::kKBytes;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int ch = 4 * kb + 2 * j + hl;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dd = 32 * db + l32;
-          const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ (dd & 7)) << 4)));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][j], o[db], 0, 0, 0);
-        }
-      }
-
-    if (more) store_tile<D>(lds + (((t - t_begin) & 1) ^ 1) * TileCfg<D>::kBufBytes, tid, kr, vr);
+  for (int t = t_begin; t < t_end; t += 2) {
+    if (t + 1 < t_end) valid1 = issue(t + 1, lds1);
+    compute_tile<D>(lds0, valid0, qreg, acc, c, l32, hl, prow);
+    wait_dma();
+    __syncthreads();
+    if (t + 1 >= t_end) break;
+    if (t + 2 < t_end) valid0 = issue(t + 2, lds0);
+    compute_tile<D>(lds1, valid1, qreg, acc, c, l32, hl, prow);
+    wait_dma();
     __syncthreads();
   }
 
   // ---- epilogue
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = acc.l + __shfl_xor(acc.l, 32);
   if (!q_ok) return;
   if (P.n_split == 1) {
     const float inv = 1.0f / l_tot;
@@ -288,10 +304,10 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnLaunch a) {
       for (int g = 0; g < 4; ++g) {
         bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(o[db][4 * g + e] * inv);
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc.o[db][4 * g + e] * inv);
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
       }
-    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (m_run + log2f(l_tot)) * kLn2;
+    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (acc.m + log2f(l_tot)) * kLn2;
   } else {
     float* part = P.part + int64_t(split) * a.part_stride;
     float* op = part + (int64_t(q) * nh + h) * D + 4 * hl;
@@ -299,12 +315,12 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnLaunch a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float4 ov = make_float4(o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]);
+        float4 ov = make_float4(acc.o[db][4 * g], acc.o[db][4 * g + 1], acc.o[db][4 * g + 2], acc.o[db][4 * g + 3]);
         *reinterpret_cast<float4*>(op + 32 * db + 8 * g) = ov;
       }
     if (hl == 0) {
       float* ml = part + a.part_ml_off + (int64_t(h) * lq + q) * 2;
-      ml[0] = m_run;
+      ml[0] = acc.m;
       ml[1] = l_tot;
     }
   }

@@ -27,6 +27,7 @@ struct ff_ctx {
   size_t anchor_off = 0, anchor_block = 0;   // anchor a: anchor_off + a*anchor_block
   size_t slot_off = 0, slot_block = 0;       // stage k, slot s: slot_off + (k*(H+1)+s)*slot_block
   size_t part_off = 0, part_bytes_per_split = 0;
+  int split = 1;                             // key-range splits per call
   // metadata
   std::vector<uint8_t> anchor_present;
   std::vector<int> next;                     // next chunk per stage
@@ -61,8 +62,20 @@ bool shape_ok(const ff_shape* s, int S, int H) {
 
 struct Layout {
   size_t anchor_off, anchor_block, slot_off, slot_block, part_off, part_per_split, total;
-  int n_anchor, n_chunk;
+  int n_anchor, n_chunk, split;
 };
+
+// Key-range splits of one call.  A function of the call's own shape only, so a
+// call gives the same bits alone or inside a grouped launch.  Splits are used
+// when heads x query tiles would leave most of the chip's 256 CUs idle.
+int split_for(const ff_shape* s) {
+  if (s->dtype != FF_BF16) return 1;
+  const int64_t lq = int64_t(s->tokens_per_latent) * s->chunk_latents;
+  const int64_t items = int64_t(s->n_heads) * ((lq + kBlockM - 1) / kBlockM);
+  int split = 1;
+  while (split < kMaxSplit && items * split < 480) split *= 2;
+  return split;
+}
 
 Layout layout_of(const ff_shape* s, int S, int H) {
   Layout L{};
@@ -75,9 +88,11 @@ Layout layout_of(const ff_shape* s, int S, int H) {
   L.slot_block = align_up(2 * nh * lq * d * esz);
   L.anchor_off = 0;
   L.slot_off = L.anchor_off + size_t(L.n_anchor) * L.anchor_block;
-  L.part_per_split = align_up(lq * nh * d * 4) + align_up(nh * lq * 2 * 4);
+  L.split = split_for(s);
+  L.part_per_split = L.split > 1 ? align_up(lq * nh * d * 4) + align_up(nh * lq * 2 * 4) : 0;
   L.part_off = L.slot_off + size_t(S) * size_t(H + 1) * L.slot_block;
-  L.total = L.part_off + size_t(kMaxSplit) * L.part_per_split;
+  // one set of split partials per pair a grouped launch can hold (one per stage)
+  L.total = L.part_off + size_t(std::min(S, kMaxPairs)) * size_t(L.split) * L.part_per_split;
   return L;
 }
 
@@ -142,17 +157,17 @@ void plan_of(const ff_ctx* c, int i, int k, ff_key_sources* p) {
 
 void seg_table_of(const ff_ctx* c, int k, const ff_key_sources& p, SegTable* t) {
   std::memset(t, 0, sizeof(*t));
-  int32_t acc = 0;
+  int32_t tiles = 0;
   for (int j = 0; j < p.n_sources; ++j) {
     const uint8_t* base = p.kind[j] == FF_SRC_ANCHOR
                               ? c->ws + c->anchor_off + size_t(p.id[j]) * c->anchor_block
                               : slot_ptr(c, k, p.id[j]);
     t->base[j] = base;
     t->n[j] = p.n_tokens[j];
-    t->start[j] = acc;
-    acc += p.n_tokens[j];
+    t->tile_start[j] = tiles;
+    tiles += (p.n_tokens[j] + kBlockN - 1) / kBlockN;
   }
-  t->start[p.n_sources] = acc;
+  t->tile_start[p.n_sources] = tiles;
   t->nseg = p.n_sources;
 }
 
@@ -170,11 +185,7 @@ void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_so
   a->scale = float(1.0 / std::sqrt(double(c->shape.head_dim)));
   a->part_stride = int64_t(c->part_bytes_per_split / 4);
   a->part_ml_off = int64_t(align_up(size_t(c->Lq) * size_t(a->nh) * size_t(a->d) * 4) / 4);
-  const int64_t items1 = int64_t(a->nh) * a->n_qtiles * n_pairs;
-  int split = 1;
-  if (c->shape.dtype == FF_BF16) {
-    while (split * 2 * n_pairs <= kMaxSplit && items1 * split < 480) split *= 2;
-  }
+  const int split = c->split;
   int32_t base = 0;
   for (int p = 0; p < n_pairs; ++p) {
     PairLaunch& pl = a->pair[p];
@@ -183,7 +194,8 @@ void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_so
     pl.lse = lse ? lse[p] : nullptr;
     seg_table_of(c, ks[p], plans[p], &pl.seg);
     pl.lk = plans[p].key_tokens;
-    const int ntiles = (pl.lk + kBlockN - 1) / kBlockN;
+    const int ntiles = pl.seg.tile_start[pl.seg.nseg];
+    pl.ntiles = ntiles;
     int sp = std::min(split, ntiles);
     pl.tiles_per_split = (ntiles + sp - 1) / sp;
     sp = (ntiles + pl.tiles_per_split - 1) / pl.tiles_per_split;   // no empty split
@@ -246,6 +258,7 @@ ff_status ff_stage_bank_create(const ff_shape* shape, int n_stages, int history,
   c->slot_block = L.slot_block;
   c->part_off = L.part_off;
   c->part_bytes_per_split = L.part_per_split;
+  c->split = L.split;
   c->anchor_present.assign(size_t(L.n_anchor), 0);
   c->next.assign(size_t(n_stages), 0);
   c->can_rewind.assign(size_t(n_stages), 0);
