@@ -51,7 +51,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="step480", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=1, help="heads in the CPU oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads in the CPU oracle sample")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed region, run a plain 256 MiB device copy (read + write of known size) "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -150,6 +153,15 @@ def main():
     pub_gbps = pub_bytes / (pub_ms * 1e-3) / 1e9
     log(f"attention kernel {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s), merge {merge_ms:.3f} ms, "
         f"publish {pub_ms * 1e3:.1f} us ({pub_gbps:.0f} GB/s), step {ms_per_step:.3f} ms")
+
+    if args.calibration_copy:
+        n = 64 << 20                                   # 64 Mi floats = 256 MiB each way
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log("calibration copy: 3 x (256 MiB read + 256 MiB write), kernel vectorized_elementwise add")
 
     cpu = None
     if not args.no_cpu_baseline:

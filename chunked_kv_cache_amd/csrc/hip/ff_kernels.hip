@@ -69,7 +69,18 @@ struct TileCfg {
   static constexpr int kChunksPerRow = D / 8;
 };
 
-__device__ __forceinline__ int krow_swz(int r) { return (r & 3) | ((r >> 1) & 4); }
+// XOR swizzles of the 16-byte chunks of an LDS row.  The lanes of one
+// ds_read_b128 are served 16 at a time from a 256-byte window (8 at a time
+// from 128 bytes on narrower LDS); with these swizzles the rows read together
+// land on distinct 16-byte bank groups in both cases.
+//   K tile row r (D = 128: 256-byte rows; D = 64: 128-byte rows)
+//   V^T tile row dd (128-byte rows)
+template <int D>
+__device__ __forceinline__ int krow_swz(int r) {
+  if (D == 128) return (r & 3) | ((r >> 1) & 4) | ((r << 1) & 8);
+  return ((r & 3) | ((r >> 1) & 4)) ^ ((r >> 2) & 1);
+}
+__device__ __forceinline__ int vrow_swz(int dd) { return (dd & 7) ^ ((dd >> 3) & 1); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef const __attribute__((address_space(1))) void glb_void;
@@ -120,7 +131,7 @@ __device__ __forceinline__ int issue_tile(const SrcCursor<D>& c, int t, uint8_t*
   for (int j = 0; j < TileCfg<D>::kKBlocks; ++j) {
     const int b = w * TileCfg<D>::kKBlocks + j;
     int r = b * TileCfg<D>::kRowsPerKBlock + lane / CPR;
-    const int ch = (lane % CPR) ^ krow_swz(r);
+    const int ch = (lane % CPR) ^ krow_swz<D>(r);
     r = r < valid ? r : 0;                           // rows past the source: any valid row
     dma16(kt + r * D + ch * 8, buf + b * 1024);
   }
@@ -130,7 +141,7 @@ __device__ __forceinline__ int issue_tile(const SrcCursor<D>& c, int t, uint8_t*
   for (int j = 0; j < TileCfg<D>::kVBlocks; ++j) {
     const int b = w * TileCfg<D>::kVBlocks + j;
     const int dd = b * 8 + lane / 8;
-    int ch = (lane & 7) ^ (dd & 7);
+    int ch = (lane & 7) ^ vrow_swz(dd);
     ch = ch * 8 < valid ? ch : 0;
     dma16(vt + int64_t(dd) * c.n + ch * 8, vbuf + b * 1024);
   }
@@ -153,7 +164,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t* buf, int valid, cons
   for (int kb = 0; kb < 2; ++kb) {
     const int row = 32 * kb + prow;
     const uint8_t* kbase = buf + row * (D * 2);
-    const int sw = krow_swz(row);
+    const int sw = krow_swz<D>(row);
     const f32x16 zero = {};
     s[kb] = zero;
 #pragma unroll
@@ -210,7 +221,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t* buf, int valid, cons
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dd = 32 * db + l32;
-        const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ (dd & 7)) << 4)));
+        const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ vrow_swz(dd)) << 4)));
         acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][j], acc.o[db], 0, 0, 0);
       }
     }
