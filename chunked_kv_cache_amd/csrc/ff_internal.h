@@ -15,7 +15,8 @@ namespace ff {
 constexpr int kMaxSeg = 12;        // <= 3 anchors + 8 history chunks + own chunk
 constexpr int kMaxPairs = 8;       // renderer calls fused into one launch
 constexpr int kMaxHistory = 8;
-constexpr int kBlockM = 128;       // query rows per attention work item
+constexpr int kBlockM = 256;       // query rows per attention work item (8 waves x 32)
+constexpr int kCUs = 256;          // MI355X compute units (one work item each)
 constexpr int kBlockN = 64;        // keys per LDS tile
 constexpr int kMaxSplit = 4;       // key-range splits per work item
 

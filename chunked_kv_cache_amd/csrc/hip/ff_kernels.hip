@@ -58,13 +58,15 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 // arrays.  The LDS layouts are XOR-swizzled for conflict-free 16-byte reads;
 // the swizzle is applied by choosing which global chunk each lane fetches.
 // --------------------------------------------------------------------------
+constexpr int kWaves = 8;          // waves per work item: 2 per SIMD, 32 queries each
+
 template <int D>
 struct TileCfg {
   static constexpr int kKBytes = kBlockN * D * 2;     // K tile [64][D]
   static constexpr int kVBytes = D * kBlockN * 2;     // V^T tile [D][64]
   static constexpr int kBufBytes = kKBytes + kVBytes;
-  static constexpr int kKBlocks = kKBytes / 1024 / 4; // 1 KB DMA blocks per wave
-  static constexpr int kVBlocks = kVBytes / 1024 / 4;
+  static constexpr int kKBlocks = kKBytes / 1024 / kWaves;   // 1 KB DMA blocks per wave
+  static constexpr int kVBlocks = kVBytes / 1024 / kWaves;
   static constexpr int kRowsPerKBlock = 1024 / (2 * D);
   static constexpr int kChunksPerRow = D / 8;
 };
@@ -148,89 +150,115 @@ __device__ __forceinline__ int issue_tile(const SrcCursor<D>& c, int t, uint8_t*
   return valid;
 }
 
-template <int D>
-struct Acc {
-  f32x16 o[D / 32];
-  float m, l;
-};
-
-// One 64-key tile from LDS: S^T, softmax update, O^T += V^T P^T.
-template <int D>
-__device__ __forceinline__ void compute_tile(const uint8_t* buf, int valid, const bf16x8 (&qreg)[D / 16],
-                                             Acc<D>& acc, float c, int l32, int hl, int prow) {
-  constexpr int KS = D / 16, DB = D / 32;
-  f32x16 s[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const int row = 32 * kb + prow;
-    const uint8_t* kbase = buf + row * (D * 2);
-    const int sw = krow_swz<D>(row);
-    const f32x16 zero = {};
-    s[kb] = zero;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch = 2 * ks + hl;
-      const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(kbase + ((ch ^ sw) << 4)));
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], s[kb], 0, 0, 0);
-    }
-  }
-  if (valid < kBlockN) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-        if (key >= valid) s[kb][r] = -INFINITY;
-      }
-  }
-  float mx = fmaxf(s[0][0], s[1][0]);
-#pragma unroll
-  for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s[0][r], s[1][r]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mx2 = mx * c;
-  if (__builtin_expect(__ballot(mx2 > acc.m + kRescaleTau) != 0, 0)) {
-    const float m_new = fmaxf(acc.m, mx2);
-    const float alpha = __builtin_amdgcn_exp2f(acc.m - m_new);
-    acc.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc.o[db][r] *= alpha;
-    acc.m = m_new;
-  }
-  const float nm = -acc.m;
-  bf16x8 pb[2][2];
-  float lsum = 0.f;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * j + e], c, nm));
-        lsum += pv;
-        pb[kb][j][e] = (__bf16)pv;
-      }
-  acc.l += lsum;
-  const uint8_t* vbase = buf + TileCfg<D>::kKBytes;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ch = 4 * kb + 2 * j + hl;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int dd = 32 * db + l32;
-        const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ vrow_swz(dd)) << 4)));
-        acc.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][j], acc.o[db], 0, 0, 0);
-      }
-    }
+// --------------------------------------------------------------------------
+// Per-wave software pipeline over the two 32-key halves of each 64-key tile.
+// While the matrix pipe runs the S^T MFMAs of the next half, the VALU does the
+// softmax of the current half (the two are independent), then the PV MFMAs of
+// the current half follow.  Two score buffers alternate roles across the
+// unrolled halves, so nothing is copied.
+// --------------------------------------------------------------------------
+// Max / sum over the two 32-lane halves (lanes l and l^32 hold the same query).
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnLaunch a) {
+struct WaveState {
+  f32x16 o[D / 32];          // O^T accumulators, one per 32-row block of d
+  float m, l;                // running max (base 2) and per-lane partial sum
+};
+
+// S^T for one 32-key half (keys 32*half .. +31 of the tile in buf).
+template <int D>
+__device__ __forceinline__ void qk_half(const uint8_t* buf, int half, const bf16x8 (&qreg)[D / 16], f32x16& s,
+                                        int hl, int prow) {
+  const int row = 32 * half + prow;
+  const uint8_t* kbase = buf + row * (D * 2);
+  const int sw = krow_swz<D>(row);
+  const f32x16 zero = {};
+  s = zero;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int ch = 2 * ks + hl;
+    const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(kbase + ((ch ^ sw) << 4)));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], s, 0, 0, 0);
+  }
+}
+
+// Register r of this lane holds key 16*(r/8) + 8*hl + r%8 of the half.
+__device__ __forceinline__ void mask_half(f32x16& s, int limit, int hl) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (16 * (r >> 3) + 8 * hl + (r & 7) >= limit) s[r] = -INFINITY;
+}
+
+__device__ __forceinline__ float rowmax_half(const f32x16& s) {
+  float a = fmaxf(s[0], s[1]);
+#pragma unroll
+  for (int r = 2; r < 16; r += 2) a = fmaxf(a, fmaxf(s[r], s[r + 1]));
+  return half_swap_max(a);
+}
+
+// Raise the running max when a half's max exceeds it by more than the
+// threshold, rescaling O and the partial sum; run before that half's exps.
+template <int D>
+__device__ __forceinline__ void rescale(float mx, float c, WaveState<D>& st) {
+  const float mx2 = mx * c;
+  if (__builtin_expect(__ballot(mx2 > st.m + kRescaleTau) != 0, 0)) {
+    const float m_new = fmaxf(st.m, mx2);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+    st.m = m_new;
+  }
+}
+
+// P = 2^(s*c - m) as bf16 B operands, and the partial row sum (branch-free).
+template <int D>
+__device__ __forceinline__ void softmax_p(const f32x16& s, float c, WaveState<D>& st, bf16x8 (&pb)[2]) {
+  const float nm = -st.m;
+  float lsum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float pv = __builtin_amdgcn_exp2f(fmaf(s[8 * j + e], c, nm));
+      lsum += pv;
+      pb[j][e] = (__bf16)pv;
+    }
+  st.l += lsum;
+}
+
+// O^T += V^T P^T for one 32-key half.
+template <int D>
+__device__ __forceinline__ void pv_half(const uint8_t* buf, int half, const bf16x8 (&pb)[2], WaveState<D>& st,
+                                        int l32, int hl) {
+  const uint8_t* vbase = buf + TileCfg<D>::kKBytes;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int ch = 4 * half + 2 * j + hl;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int dd = 32 * db + l32;
+      const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ vrow_swz(dd)) << 4)));
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[j], st.o[db], 0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLaunch a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds0[TileCfg<D>::kBufBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t lds1[TileCfg<D>::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[TileCfg<D>::kBufBytes];
   constexpr int KS = D / 16;       // MFMA k-steps over head_dim
   constexpr int DB = D / 32;       // 32-row blocks of O^T
 
@@ -269,13 +297,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnLaunch a) {
   // Row of the K tile this lane feeds as A operand (bits 2 and 3 swapped).
   const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
 
-  Acc<D> acc;
+  WaveState<D> st;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc.o[db][r] = 0.f;
-  acc.m = -INFINITY;
-  acc.l = 0.f;
+    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
+  st.m = -INFINITY;
+  st.l = 0.f;
 
   SrcCursor<D> cur;
   {
@@ -288,23 +316,53 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnLaunch a) {
     return issue_tile<D>(cur, t, buf, w, lane);
   };
 
-  int valid0 = issue(t_begin, lds0), valid1 = 0;
+  f32x16 sa, sb;         // scores of the half awaiting softmax / being computed
+  bf16x8 pb[2];
+  int valid[3];
+  valid[0] = issue(t_begin, lds0);
+  if (t_begin + 1 < t_end) valid[1] = issue(t_begin + 1, lds1);
   wait_dma();
   __syncthreads();
-  for (int t = t_begin; t < t_end; t += 2) {
-    if (t + 1 < t_end) valid1 = issue(t + 1, lds1);
-    compute_tile<D>(lds0, valid0, qreg, acc, c, l32, hl, prow);
-    wait_dma();
-    __syncthreads();
+  qk_half<D>(lds0, 0, qreg, sa, hl, prow);
+  if (valid[0] < 32) mask_half(sa, valid[0], hl);
+  rescale<D>(rowmax_half(sa), c, st);
+
+  // Tile t is in B (landed); B1 receives tile t+1, B2 is free for tile t+2.
+  // Invariant at entry: sa = masked scores of half 0 of tile t, max applied.
+  auto tile = [&](const uint8_t* B, const uint8_t* B1, uint8_t* B2, int t, int v0, int v1, int v2) {
+    // half 0: S^T(half 1) and softmax(half 0) interleave; then PV(half 0)
+    qk_half<D>(B, 1, qreg, sb, hl, prow);
+    softmax_p<D>(sa, c, st, pb);
+    pv_half<D>(B, 0, pb, st, l32, hl);
+    if (valid[v0] < kBlockN) mask_half(sb, valid[v0] - 32, hl);
+    rescale<D>(rowmax_half(sb), c, st);
+    // half 1: S^T(tile t+1, half 0) and softmax(half 1); then PV(half 1).
+    // On the last tile the S^T of B1 is computed on stale data and dropped.
+    const bool more = t + 1 < t_end;
+    if (more) {
+      wait_dma();
+      __syncthreads();
+      if (t + 2 < t_end) valid[v2] = issue(t + 2, B2);
+    }
+    qk_half<D>(B1, 0, qreg, sa, hl, prow);
+    softmax_p<D>(sb, c, st, pb);
+    pv_half<D>(B, 1, pb, st, l32, hl);
+    if (more) {
+      if (valid[v1] < 32) mask_half(sa, valid[v1], hl);
+      rescale<D>(rowmax_half(sa), c, st);
+    }
+  };
+
+  for (int t = t_begin; t < t_end; t += 3) {
+    tile(lds0, lds1, lds2, t, 0, 1, 2);
     if (t + 1 >= t_end) break;
-    if (t + 2 < t_end) valid0 = issue(t + 2, lds0);
-    compute_tile<D>(lds1, valid1, qreg, acc, c, l32, hl, prow);
-    wait_dma();
-    __syncthreads();
+    tile(lds1, lds2, lds0, t + 1, 1, 2, 0);
+    if (t + 2 >= t_end) break;
+    tile(lds2, lds0, lds1, t + 2, 2, 0, 1);
   }
 
   // ---- epilogue
-  const float l_tot = acc.l + __shfl_xor(acc.l, 32);
+  const float l_tot = half_swap_sum(st.l);
   if (!q_ok) return;
   if (P.n_split == 1) {
     const float inv = 1.0f / l_tot;
@@ -315,10 +373,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnLaunch a) {
       for (int g = 0; g < 4; ++g) {
         bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(acc.o[db][4 * g + e] * inv);
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(st.o[db][4 * g + e] * inv);
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
       }
-    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (acc.m + log2f(l_tot)) * kLn2;
+    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (st.m + log2f(l_tot)) * kLn2;
   } else {
     float* part = P.part + int64_t(split) * a.part_stride;
     float* op = part + (int64_t(q) * nh + h) * D + 4 * hl;
@@ -326,12 +384,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(const AttnLaunch a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float4 ov = make_float4(acc.o[db][4 * g], acc.o[db][4 * g + 1], acc.o[db][4 * g + 2], acc.o[db][4 * g + 3]);
+        float4 ov = make_float4(st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2], st.o[db][4 * g + 3]);
         *reinterpret_cast<float4*>(op + 32 * db + 8 * g) = ov;
       }
     if (hl == 0) {
       float* ml = part + a.part_ml_off + (int64_t(h) * lq + q) * 2;
-      ml[0] = acc.m;
+      ml[0] = st.m;
       ml[1] = l_tot;
     }
   }
@@ -552,8 +610,8 @@ int dev_launch_attention(const AttnLaunch& a, void* stream, Profiler* prof) {
   }
   {
     Timed tm(prof, kAttn, s);
-    if (a.d == 64) hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(a.total_items), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(a.total_items), dim3(256), 0, s, a);
+    if (a.d == 64) hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(a.total_items), dim3(kWaves * 64), 0, s, a);
+    else hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(a.total_items), dim3(kWaves * 64), 0, s, a);
   }
   if (launch_ok()) return FF_E_HIP;
   bool any_split = false;

@@ -66,15 +66,20 @@ struct Layout {
 };
 
 // Key-range splits of one call.  A function of the call's own shape only, so a
-// call gives the same bits alone or inside a grouped launch.  Splits are used
-// when heads x query tiles would leave most of the chip's 256 CUs idle.
+// call gives the same bits alone or inside a grouped launch.  One work item
+// runs per CU; the split minimises rounds-of-items per unit of work,
+// ceil(items * s / CUs) / s, preferring fewer splits on ties.
 int split_for(const ff_shape* s) {
   if (s->dtype != FF_BF16) return 1;
   const int64_t lq = int64_t(s->tokens_per_latent) * s->chunk_latents;
   const int64_t items = int64_t(s->n_heads) * ((lq + kBlockM - 1) / kBlockM);
-  int split = 1;
-  while (split < kMaxSplit && items * split < 480) split *= 2;
-  return split;
+  int best = 1;
+  double best_cost = 1e30;
+  for (int sp = 1; sp <= kMaxSplit; ++sp) {
+    const double cost = double((items * sp + kCUs - 1) / kCUs) / sp;
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = sp; }
+  }
+  return best;
 }
 
 Layout layout_of(const ff_shape* s, int S, int H) {
