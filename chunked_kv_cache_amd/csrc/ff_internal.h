@@ -18,7 +18,6 @@ constexpr int kMaxHistory = 8;
 constexpr int kBlockM = 256;       // query rows per attention work item (8 waves x 32)
 constexpr int kCUs = 256;          // MI355X compute units (one work item each)
 constexpr int kBlockN = 64;        // keys per LDS tile
-constexpr int kMaxSplit = 4;       // key-range splits per work item
 
 // One key source as the attention kernel sees it.  `base` points at the
 // source's block in the workspace: K head-major [nh][n][d] followed directly by
@@ -33,17 +32,20 @@ struct SegTable {
   int32_t nseg;
 };
 
+// Attention work of one call ("pair" = chunk i at stage k).  Work item =
+// (head, 256-query tile); each item runs over all of the call's key tiles.
+// The (item x key tile) units of a call are split evenly and contiguously
+// over the persistent workgroups (stream-K); an item cut between workgroups
+// leaves partial results in `part` that the merge kernel combines.
 struct PairLaunch {
   const void* q;                   // [Lq][nh][d] token-major
   void* o;                         // [Lq][nh][d] token-major
   float* lse;                      // [nh][Lq] or null
-  float* part;                     // split-K partials of this pair (or null)
+  float* part;                     // partial slots of this call: n_wg x 2
   SegTable seg;
   int32_t lk;                      // key tokens
   int32_t ntiles;                  // 64-key tiles (sources padded to whole tiles)
-  int32_t n_split;
-  int32_t tiles_per_split;
-  int32_t item_base;               // first work item of this pair
+  int32_t n_items;                 // nh x n_qtiles
 };
 
 struct AttnLaunch {
@@ -51,11 +53,10 @@ struct AttnLaunch {
   int32_t n_pairs;
   int32_t nh, d, lq;
   int32_t n_qtiles;
-  int32_t total_items;
+  int32_t n_wg;                    // persistent workgroups (one per CU)
   int32_t dtype;                   // ff_dtype
   float scale;                     // 1/sqrt(d)
-  int64_t part_stride;             // floats between the partials of two splits
-  int64_t part_ml_off;             // floats from a split's O partial to its (m, l)
+  int64_t slot_floats;             // floats per partial slot: O [BM][d], m [BM], l [BM]
 };
 
 // Layout copies between token-major rows and bank blocks.  A job moves `nseg`

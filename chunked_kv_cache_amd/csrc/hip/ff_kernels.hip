@@ -5,7 +5,7 @@
 //                 gathered from the anchor bank and the stage ring through the
 //                 call's key-source table into LDS (no concatenation copy).
 //  attn_f32<D>    plain fp32 path (one lane per query row and head).
-//  merge_splits   LSE merge of key-range splits.
+//  merge_pieces   LSE merge of the items the stream-K partition cut.
 //  publish        token-major K/V -> bank block (K head-major, V transposed).
 //  unpack         bank block -> token-major K/V (read-out of B_k).
 //
@@ -91,8 +91,11 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
   __builtin_amdgcn_global_load_lds((glb_void*)(g), (lds_void*)(l), 16, 0, 0);
 }
 
-// Wait until this wave's outstanding global->LDS copies have landed.
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// Wait until this wave's outstanding global->LDS copies have landed
+// (vmcnt(0)), or all but the newest N (vmcnt(N), N < 16).
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+template <int N>
+__device__ __forceinline__ void wait_dma_but() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
 
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -254,29 +257,24 @@ __device__ __forceinline__ void pv_half(const uint8_t* buf, int half, const bf16
   }
 }
 
+// One piece of work: item (head h, query tile qt) over key tiles [t_begin,
+// t_end).  A whole item writes O and LSE; a piece writes its unnormalised O,
+// running max and sum to `slot` for the merge kernel.
 template <int D>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLaunch a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TileCfg<D>::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TileCfg<D>::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[TileCfg<D>::kBufBytes];
+__device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& P, int item, int t_begin, int t_end,
+                                         float* slot, uint8_t* lds0, uint8_t* lds1, uint8_t* lds2, uint8_t* lds3) {
   constexpr int KS = D / 16;       // MFMA k-steps over head_dim
   constexpr int DB = D / 32;       // 32-row blocks of O^T
-
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  int p = 0;
-  while (p + 1 < a.n_pairs && item >= a.pair[p + 1].item_base) ++p;
-  const PairLaunch& P = a.pair[p];
+  constexpr int kDmaPerTile = TileCfg<D>::kKBlocks + TileCfg<D>::kVBlocks;   // per wave
   const int nh = a.nh, lq = a.lq;
-  int local = item - P.item_base;
-  const int qt = local % a.n_qtiles;
-  local /= a.n_qtiles;
-  const int h = local % nh;
-  const int split = local / nh;
+  const int qt = item % a.n_qtiles;
+  const int h = item / a.n_qtiles;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int q = qt * kBlockM + w * 32 + l32;
+  const int row = w * 32 + l32;                  // query row within the tile
+  const int q = qt * kBlockM + row;
   const bool q_ok = q < lq;
 
   // Q^T as the B operand: lane holds Q[q][16*ks + 8*hl .. +7].
@@ -291,8 +289,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLau
     }
   }
 
-  const int t_begin = split * P.tiles_per_split;
-  const int t_end = min(P.ntiles, t_begin + P.tiles_per_split);
   const float c = a.scale * kLog2e;
   // Row of the K tile this lane feeds as A operand (bits 2 and 3 swapped).
   const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
@@ -318,18 +314,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLau
 
   f32x16 sa, sb;         // scores of the half awaiting softmax / being computed
   bf16x8 pb[2];
-  int valid[3];
+  int valid[4];
+  __syncthreads();       // the previous piece's reads of the buffers are done
   valid[0] = issue(t_begin, lds0);
   if (t_begin + 1 < t_end) valid[1] = issue(t_begin + 1, lds1);
-  wait_dma();
+  if (t_begin + 2 < t_end) valid[2] = issue(t_begin + 2, lds2);
+  if (t_begin + 2 < t_end) wait_dma_but<2 * kDmaPerTile>();
+  else if (t_begin + 1 < t_end) wait_dma_but<kDmaPerTile>();
+  else wait_dma();
   __syncthreads();
   qk_half<D>(lds0, 0, qreg, sa, hl, prow);
   if (valid[0] < 32) mask_half(sa, valid[0], hl);
   rescale<D>(rowmax_half(sa), c, st);
 
-  // Tile t is in B (landed); B1 receives tile t+1, B2 is free for tile t+2.
+  // Tile t is in B (landed); B1 holds tile t+1 and B2 tile t+2 (both may still
+  // be landing); B3 is free for tile t+3.  Copies run two tiles ahead.
   // Invariant at entry: sa = masked scores of half 0 of tile t, max applied.
-  auto tile = [&](const uint8_t* B, const uint8_t* B1, uint8_t* B2, int t, int v0, int v1, int v2) {
+  auto tile = [&](const uint8_t* B, const uint8_t* B1, uint8_t* B3, int t, int v0, int v1, int v3) {
     // half 0: S^T(half 1) and softmax(half 0) interleave; then PV(half 0)
     qk_half<D>(B, 1, qreg, sb, hl, prow);
     softmax_p<D>(sa, c, st, pb);
@@ -340,9 +341,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLau
     // On the last tile the S^T of B1 is computed on stale data and dropped.
     const bool more = t + 1 < t_end;
     if (more) {
-      wait_dma();
+      if (t + 2 < t_end) wait_dma_but<kDmaPerTile>();   // tile t+1 landed, t+2 may fly
+      else wait_dma();
       __syncthreads();
-      if (t + 2 < t_end) valid[v2] = issue(t + 2, B2);
+      if (t + 3 < t_end) valid[v3] = issue(t + 3, B3);
     }
     qk_half<D>(B1, 0, qreg, sa, hl, prow);
     softmax_p<D>(sb, c, st, pb);
@@ -353,18 +355,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLau
     }
   };
 
-  for (int t = t_begin; t < t_end; t += 3) {
-    tile(lds0, lds1, lds2, t, 0, 1, 2);
+  for (int t = t_begin; t < t_end; t += 4) {
+    tile(lds0, lds1, lds3, t, 0, 1, 3);
     if (t + 1 >= t_end) break;
     tile(lds1, lds2, lds0, t + 1, 1, 2, 0);
     if (t + 2 >= t_end) break;
-    tile(lds2, lds0, lds1, t + 2, 2, 0, 1);
+    tile(lds2, lds3, lds1, t + 2, 2, 3, 1);
+    if (t + 3 >= t_end) break;
+    tile(lds3, lds0, lds2, t + 3, 3, 0, 2);
   }
 
   // ---- epilogue
   const float l_tot = half_swap_sum(st.l);
   if (!q_ok) return;
-  if (P.n_split == 1) {
+  if (!slot) {
     const float inv = 1.0f / l_tot;
     __bf16* op = static_cast<__bf16*>(P.o) + (int64_t(q) * nh + h) * D + 4 * hl;
 #pragma unroll
@@ -378,8 +382,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLau
       }
     if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (st.m + log2f(l_tot)) * kLn2;
   } else {
-    float* part = P.part + int64_t(split) * a.part_stride;
-    float* op = part + (int64_t(q) * nh + h) * D + 4 * hl;
+    float* op = slot + row * D + 4 * hl;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -388,47 +391,97 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLau
         *reinterpret_cast<float4*>(op + 32 * db + 8 * g) = ov;
       }
     if (hl == 0) {
-      float* ml = part + a.part_ml_off + (int64_t(h) * lq + q) * 2;
-      ml[0] = st.m;
-      ml[1] = l_tot;
+      slot[kBlockM * D + row] = st.m;
+      slot[kBlockM * D + kBlockM + row] = l_tot;
+    }
+  }
+}
+
+// Schedule of one call over n_wg persistent workgroups (one per CU).
+// Items run whole in full rounds (workgroup g takes item r*n_wg + g, so the
+// workgroups of an XCD stream one head's K/V in lockstep).  The rem items of
+// the last, partial round are cut at key tile F: workgroup g < rem runs item g
+// over [0, F) and the spare workgroups run the tails [F, ntiles), k items each,
+// with F chosen so that k tails take about as long as one head: F =
+// ceil(k * ntiles / (k + 1)).  Cut items leave two partials for the merge.
+struct RemSplit {
+  int full, rem, k, F;
+};
+__host__ __device__ inline RemSplit rem_split(int n_items, int ntiles, int n_wg) {
+  RemSplit r;
+  r.full = n_items / n_wg;
+  r.rem = n_items % n_wg;
+  r.k = r.rem ? (r.rem + (n_wg - r.rem) - 1) / (n_wg - r.rem) : 0;
+  r.F = r.rem ? (r.k * ntiles + r.k) / (r.k + 1) : ntiles;   // ceil(k*ntiles/(k+1))
+  if (r.F > ntiles) r.F = ntiles;
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLaunch a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TileCfg<D>::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TileCfg<D>::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds2[TileCfg<D>::kBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds3[TileCfg<D>::kBufBytes];
+  // Consecutive workgroup ids sit on one XCD (shared L2).
+  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  for (int p = 0; p < a.n_pairs; ++p) {
+    const PairLaunch& P = a.pair[p];
+    const RemSplit rs = rem_split(P.n_items, P.ntiles, a.n_wg);
+    for (int r = 0; r < rs.full; ++r) run_item<D>(a, P, r * a.n_wg + g, 0, P.ntiles, nullptr, lds0, lds1, lds2, lds3);
+    if (rs.rem == 0) continue;
+    const int base = rs.full * a.n_wg;
+    const bool cut = rs.F < P.ntiles;
+    if (g < rs.rem) {
+      run_item<D>(a, P, base + g, 0, rs.F, cut ? P.part + int64_t(g) * 2 * a.slot_floats : nullptr, lds0, lds1,
+                  lds2, lds3);
+    } else if (cut) {
+      const int j = g - rs.rem;
+      const int i_end = min(rs.rem, (j + 1) * rs.k);
+      for (int i = j * rs.k; i < i_end; ++i)
+        run_item<D>(a, P, base + i, rs.F, P.ntiles, P.part + (int64_t(i) * 2 + 1) * a.slot_floats, lds0, lds1, lds2,
+                    lds3);
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// Split merge: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// One thread per (pair, query, head, 4 head-dim values).
+// Merge of the items cut in the last round: O = sum_j 2^(m_j - M) O_j /
+// sum_j 2^(m_j - M) l_j over the head piece (j = 0) and the tail piece (j = 1).
+// One block per cut item and call; D/4 consecutive threads share a query row,
+// each taking 4 head-dim values, so partial reads and O writes are coalesced.
 // --------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void merge_splits_kernel(const AttnLaunch a) {
-  const int64_t per_pair = int64_t(a.lq) * a.nh * (D / 4);
-  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int p = blockIdx.y;
-  const PairLaunch& P = a.pair[p];
-  if (P.n_split <= 1 || gid >= per_pair) return;
-  const int d4 = int(gid % (D / 4));
-  const int64_t row = gid / (D / 4);            // q * nh + h
-  const int h = int(row % a.nh);
-  const int q = int(row / a.nh);
-  float M = -INFINITY;
-  for (int s = 0; s < P.n_split; ++s)
-    M = fmaxf(M, P.part[s * a.part_stride + a.part_ml_off + (int64_t(h) * a.lq + q) * 2]);
-  float L = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < P.n_split; ++s) {
-    const float* part = P.part + s * a.part_stride;
-    const float* ml = part + a.part_ml_off + (int64_t(h) * a.lq + q) * 2;
-    const float wgt = __builtin_amdgcn_exp2f(ml[0] - M);
-    L += wgt * ml[1];
-    const float4 ov = *reinterpret_cast<const float4*>(part + row * D + 4 * d4);
-    acc.x += wgt * ov.x; acc.y += wgt * ov.y; acc.z += wgt * ov.z; acc.w += wgt * ov.w;
+__global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
+  constexpr int TPR = D / 4;                     // threads per row
+  constexpr int RPP = 256 / TPR;                 // rows per pass
+  const PairLaunch& P = a.pair[blockIdx.y];
+  const RemSplit rs = rem_split(P.n_items, P.ntiles, a.n_wg);
+  const int i = blockIdx.x;
+  if (i >= rs.rem || rs.F >= P.ntiles) return;
+  const int item = rs.full * a.n_wg + i;
+  const int qt = item % a.n_qtiles, h = item / a.n_qtiles;
+  const float* s0 = P.part + int64_t(i) * 2 * a.slot_floats;
+  const float* s1 = s0 + a.slot_floats;
+  const int c4 = threadIdx.x % TPR;
+  for (int row = threadIdx.x / TPR; row < kBlockM; row += RPP) {
+    const int q = qt * kBlockM + row;
+    if (q >= a.lq) break;
+    const float m0 = s0[kBlockM * D + row], m1 = s1[kBlockM * D + row];
+    const float M = fmaxf(m0, m1);
+    const float w0 = __builtin_amdgcn_exp2f(m0 - M), w1 = __builtin_amdgcn_exp2f(m1 - M);
+    const float L = w0 * s0[kBlockM * D + kBlockM + row] + w1 * s1[kBlockM * D + kBlockM + row];
+    const float inv = 1.0f / L;
+    const float4 x = reinterpret_cast<const float4*>(s0 + row * D)[c4];
+    const float4 y = reinterpret_cast<const float4*>(s1 + row * D)[c4];
+    bf16x4 ov;
+    ov[0] = (__bf16)((w0 * x.x + w1 * y.x) * inv);
+    ov[1] = (__bf16)((w0 * x.y + w1 * y.y) * inv);
+    ov[2] = (__bf16)((w0 * x.z + w1 * y.z) * inv);
+    ov[3] = (__bf16)((w0 * x.w + w1 * y.w) * inv);
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + (int64_t(q) * a.nh + h) * D + 4 * c4) = ov;
+    if (P.lse && c4 == 0) P.lse[int64_t(h) * a.lq + q] = (M + log2f(L)) * kLn2;
   }
-  const float inv = 1.0f / L;
-  bf16x4 out;
-  out[0] = (__bf16)(acc.x * inv); out[1] = (__bf16)(acc.y * inv);
-  out[2] = (__bf16)(acc.z * inv); out[3] = (__bf16)(acc.w * inv);
-  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + row * D + 4 * d4) = out;
-  if (P.lse && d4 == 0) P.lse[int64_t(h) * a.lq + q] = (M + log2f(L)) * kLn2;
 }
 
 // --------------------------------------------------------------------------
@@ -610,21 +663,23 @@ int dev_launch_attention(const AttnLaunch& a, void* stream, Profiler* prof) {
   }
   {
     Timed tm(prof, kAttn, s);
-    if (a.d == 64) hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(a.total_items), dim3(kWaves * 64), 0, s, a);
-    else hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(a.total_items), dim3(kWaves * 64), 0, s, a);
+    if (a.d == 64) hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(a.n_wg), dim3(kWaves * 64), 0, s, a);
+    else hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(a.n_wg), dim3(kWaves * 64), 0, s, a);
   }
   if (launch_ok()) return FF_E_HIP;
-  bool any_split = false;
-  for (int p = 0; p < a.n_pairs; ++p) any_split |= a.pair[p].n_split > 1;
-  if (any_split) {
+  {
     Timed tm(prof, kMerge, s);
-    const int64_t n = int64_t(a.lq) * a.nh * (a.d / 4);
-    dim3 grid(unsigned((n + 255) / 256), unsigned(a.n_pairs));
-    if (a.d == 64) hipLaunchKernelGGL(merge_splits_kernel<64>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(merge_splits_kernel<128>, grid, dim3(256), 0, s, a);
-    return launch_ok();
+    int max_rem = 0;
+    for (int p = 0; p < a.n_pairs; ++p) {
+      const RemSplit rs = rem_split(a.pair[p].n_items, a.pair[p].ntiles, a.n_wg);
+      if (rs.F < a.pair[p].ntiles && rs.rem > max_rem) max_rem = rs.rem;
+    }
+    if (max_rem == 0) return 0;
+    dim3 grid(unsigned(max_rem), unsigned(a.n_pairs));
+    if (a.d == 64) hipLaunchKernelGGL(merge_pieces_kernel<64>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(merge_pieces_kernel<128>, grid, dim3(256), 0, s, a);
   }
-  return 0;
+  return launch_ok();
 }
 
 template <bool kPublish>

@@ -54,18 +54,18 @@ void ffstub_counts(int* attn, int* publish, int* anchor, int* unpack) {
 }
 // Key-source table of pair p of the last attention launch, as byte offsets
 // from `ws` and token counts; returns the number of sources.
-int ffstub_last_segments(int p, const void* ws, long long* offsets, int* n_tokens, int* lk, int* n_split) {
+int ffstub_last_segments(int p, const void* ws, long long* offsets, int* n_tokens, int* lk, int* ntiles) {
   const ff::PairLaunch& P = ff::g_last_attn.pair[p];
   for (int s = 0; s < P.seg.nseg; ++s) {
     offsets[s] = static_cast<const char*>(P.seg.base[s]) - static_cast<const char*>(ws);
     n_tokens[s] = P.seg.n[s];
   }
   *lk = P.lk;
-  *n_split = P.n_split;
+  *ntiles = P.ntiles;
   return P.seg.nseg;
 }
-int ffstub_last_attn_pairs(int* total_items) {
-  *total_items = ff::g_last_attn.total_items;
+int ffstub_last_attn_pairs(int* n_wg) {
+  *n_wg = ff::g_last_attn.n_wg;
   return ff::g_last_attn.n_pairs;
 }
 // Destination block of job j of the last copy launch, as a byte offset from ws.

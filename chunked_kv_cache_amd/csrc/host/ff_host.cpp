@@ -26,8 +26,7 @@ struct ff_ctx {
   // workspace regions (byte offsets from ws)
   size_t anchor_off = 0, anchor_block = 0;   // anchor a: anchor_off + a*anchor_block
   size_t slot_off = 0, slot_block = 0;       // stage k, slot s: slot_off + (k*(H+1)+s)*slot_block
-  size_t part_off = 0, part_bytes_per_split = 0;
-  int split = 1;                             // key-range splits per call
+  size_t part_off = 0, part_slot_bytes = 0;  // stream-K partial slots
   // metadata
   std::vector<uint8_t> anchor_present;
   std::vector<int> next;                     // next chunk per stage
@@ -61,26 +60,9 @@ bool shape_ok(const ff_shape* s, int S, int H) {
 }
 
 struct Layout {
-  size_t anchor_off, anchor_block, slot_off, slot_block, part_off, part_per_split, total;
-  int n_anchor, n_chunk, split;
+  size_t anchor_off, anchor_block, slot_off, slot_block, part_off, part_slot, total;
+  int n_anchor, n_chunk;
 };
-
-// Key-range splits of one call.  A function of the call's own shape only, so a
-// call gives the same bits alone or inside a grouped launch.  One work item
-// runs per CU; the split minimises rounds-of-items per unit of work,
-// ceil(items * s / CUs) / s, preferring fewer splits on ties.
-int split_for(const ff_shape* s) {
-  if (s->dtype != FF_BF16) return 1;
-  const int64_t lq = int64_t(s->tokens_per_latent) * s->chunk_latents;
-  const int64_t items = int64_t(s->n_heads) * ((lq + kBlockM - 1) / kBlockM);
-  int best = 1;
-  double best_cost = 1e30;
-  for (int sp = 1; sp <= kMaxSplit; ++sp) {
-    const double cost = double((items * sp + kCUs - 1) / kCUs) / sp;
-    if (cost < best_cost - 1e-9) { best_cost = cost; best = sp; }
-  }
-  return best;
-}
 
 Layout layout_of(const ff_shape* s, int S, int H) {
   Layout L{};
@@ -93,11 +75,11 @@ Layout layout_of(const ff_shape* s, int S, int H) {
   L.slot_block = align_up(2 * nh * lq * d * esz);
   L.anchor_off = 0;
   L.slot_off = L.anchor_off + size_t(L.n_anchor) * L.anchor_block;
-  L.split = split_for(s);
-  L.part_per_split = L.split > 1 ? align_up(lq * nh * d * 4) + align_up(nh * lq * 2 * 4) : 0;
+  // Stream-K partial slots (bf16 path): 2 per workgroup per call that a
+  // grouped launch can hold (one call per stage).
+  L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(kBlockM) * (d + 2) * 4) : 0;
   L.part_off = L.slot_off + size_t(S) * size_t(H + 1) * L.slot_block;
-  // one set of split partials per pair a grouped launch can hold (one per stage)
-  L.total = L.part_off + size_t(std::min(S, kMaxPairs)) * size_t(L.split) * L.part_per_split;
+  L.total = L.part_off + size_t(std::min(S, kMaxPairs)) * size_t(kCUs) * 2 * L.part_slot;
   return L;
 }
 
@@ -176,8 +158,10 @@ void seg_table_of(const ff_ctx* c, int k, const ff_key_sources& p, SegTable* t) 
   t->nseg = p.n_sources;
 }
 
-// Work decomposition: items = heads x query tiles (x key splits).  Splits
-// are used only when the unsplit grid would leave most of the chip idle.
+// Work decomposition: items = heads x 256-query tiles; the (item x key tile)
+// units of each call are spread evenly over one persistent workgroup per CU.
+// The partition of a call depends only on that call, so it gives the same bits
+// alone or inside a grouped launch.
 void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_sources* plans,
                     const void* const* Q, void* const* O, float* const* lse, AttnLaunch* a) {
   std::memset(a, 0, sizeof(*a));
@@ -186,12 +170,10 @@ void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_so
   a->d = c->shape.head_dim;
   a->lq = int32_t(c->Lq);
   a->n_qtiles = int32_t((c->Lq + kBlockM - 1) / kBlockM);
+  a->n_wg = kCUs;
   a->dtype = c->shape.dtype;
   a->scale = float(1.0 / std::sqrt(double(c->shape.head_dim)));
-  a->part_stride = int64_t(c->part_bytes_per_split / 4);
-  a->part_ml_off = int64_t(align_up(size_t(c->Lq) * size_t(a->nh) * size_t(a->d) * 4) / 4);
-  const int split = c->split;
-  int32_t base = 0;
+  a->slot_floats = int64_t(c->part_slot_bytes / 4);
   for (int p = 0; p < n_pairs; ++p) {
     PairLaunch& pl = a->pair[p];
     pl.q = Q[p];
@@ -199,18 +181,12 @@ void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_so
     pl.lse = lse ? lse[p] : nullptr;
     seg_table_of(c, ks[p], plans[p], &pl.seg);
     pl.lk = plans[p].key_tokens;
-    const int ntiles = pl.seg.tile_start[pl.seg.nseg];
-    pl.ntiles = ntiles;
-    int sp = std::min(split, ntiles);
-    pl.tiles_per_split = (ntiles + sp - 1) / sp;
-    sp = (ntiles + pl.tiles_per_split - 1) / pl.tiles_per_split;   // no empty split
-    pl.n_split = sp;
-    pl.part = sp > 1 ? reinterpret_cast<float*>(c->ws + c->part_off + size_t(p) * split * c->part_bytes_per_split)
-                     : nullptr;
-    pl.item_base = base;
-    base += a->nh * a->n_qtiles * sp;
+    pl.ntiles = pl.seg.tile_start[pl.seg.nseg];
+    pl.n_items = a->nh * a->n_qtiles;
+    pl.part = c->part_slot_bytes
+                  ? reinterpret_cast<float*>(c->ws + c->part_off + size_t(p) * size_t(kCUs) * 2 * c->part_slot_bytes)
+                  : nullptr;
   }
-  a->total_items = base;
 }
 
 }  // namespace
@@ -262,8 +238,7 @@ ff_status ff_stage_bank_create(const ff_shape* shape, int n_stages, int history,
   c->slot_off = L.slot_off;
   c->slot_block = L.slot_block;
   c->part_off = L.part_off;
-  c->part_bytes_per_split = L.part_per_split;
-  c->split = L.split;
+  c->part_slot_bytes = L.part_slot;
   c->anchor_present.assign(size_t(L.n_anchor), 0);
   c->next.assign(size_t(n_stages), 0);
   c->can_rewind.assign(size_t(n_stages), 0);

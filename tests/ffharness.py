@@ -12,7 +12,17 @@ import oracle as orc
 import synthetic as syn
 from chunked_kv_cache_amd import ff
 
-TOL = {"bf16": 2e-2, "f32": 1e-4}          # O max-abs gates
+TOL = {"bf16": 2e-2, "f32": 1e-4}          # O max-abs gates (N(0,1) workloads, |O| << 1)
+
+
+def bf16_rounding_bound(O_ref: np.ndarray, V_keys: float) -> float:
+    """Worst-case |dO| of the bf16 path from its two roundings: each softmax
+    weight p is rounded to bf16 before the PV product (relative error <= 2^-9,
+    so |dO| <= 2^-9 max|V|) and O is rounded to bf16 (<= half an ulp, which is
+    <= 2^-8 |O|).  fp32 accumulation adds far less; 10% margin."""
+    return 1.1 * (2.0 ** -8 * float(np.abs(O_ref).max()) + 2.0 ** -9 * float(V_keys))
+
+
 LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
 RELF_TOL = {"bf16": 1e-2, "f32": 1e-5}     # relative Frobenius (diagnostic gate)
 
@@ -82,6 +92,7 @@ class Pair:
                 self.banks.workspace[: self.banks.ws_bytes // 4 * 4].view(torch.float32).fill_(float("nan"))
         self.ro = orc.Rollout(self.cfg)
         self.inputs = {}
+        self.vmax = {}                       # max |V| per key source, for the rounding bound
         self.stats = Stats()
         self.oracle_compute = oracle_compute
 
@@ -94,7 +105,10 @@ class Pair:
         for blk in orc.planner_blocks(self.cfg):
             K, V = syn.anchor_kv(T=c.T, n_heads=c.nh, head_dim=c.d, anchors=blk, seed=c.seed, dtype=c.dtype)
             ff.ff_anchor_bank_publish(self.ctx, blk[0], len(blk), to_device(K, c.dtype), to_device(V, c.dtype))
-            self.ro.publish_anchors(blk[0], syn.as_f64(K, c.dtype), syn.as_f64(V, c.dtype))
+            V64 = syn.as_f64(V, c.dtype)
+            self.ro.publish_anchors(blk[0], syn.as_f64(K, c.dtype), V64)
+            for j, a in enumerate(blk):
+                self.vmax[("anchor", a)] = float(np.abs(V64[j * c.T:(j + 1) * c.T]).max())
 
     def gen(self, i, k):
         c = self.case
@@ -125,6 +139,9 @@ class Pair:
         results = []
         for j, ((i, k), h) in enumerate(zip(pairs, host)):
             q64, k64, v64 = (syn.as_f64(x, c.dtype) for x in h)
+            self.vmax[("history", (i, k))] = float(np.abs(v64).max())
+            vkeys = max(self.vmax[("anchor", x)] if kind == "anchor" else self.vmax[("history", (x, k))]
+                        for kind, x in self.ro.key_sources(i, k))
             O_ref, L_ref = self.ro.render_attend(i, k, q64, k64, v64, rows=rows, compute=self.oracle_compute)
             self.inputs[(i, k)] = (h[1], h[2])
             if self.oracle_compute:
@@ -132,7 +149,11 @@ class Pair:
                 L = lses[j].cpu().numpy().astype(np.float64)
                 if rows is not None:
                     O, L = O[rows], L[:, rows]
-                self._compare(O, L, O_ref, L_ref, controls[j] if control else None)
+                tol = TOL[c.dtype]
+                if c.dtype == "bf16":
+                    # stress cases with |O| >> 1 (peaked softmax): gate on the rounding bound
+                    tol = max(tol, bf16_rounding_bound(O_ref, vkeys))
+                self._compare(O, L, O_ref, L_ref, controls[j] if control else None, tol)
                 results.append((O, O_ref))
             if check_bank:
                 self.check_bank(k)
@@ -149,7 +170,7 @@ class Pair:
         O, _ = orc.attention(q, Kc[n_anchor_tok:], Vc[n_anchor_tok:], self.cfg.scale)
         return O
 
-    def _compare(self, O, L, O_ref, L_ref, O_ctrl):
+    def _compare(self, O, L, O_ref, L_ref, O_ctrl, tol):
         dt = self.case.dtype
         assert np.all(np.isfinite(O)), "non-finite output"
         err = np.abs(O - O_ref).max()
@@ -160,7 +181,7 @@ class Pair:
         st.max_rel_fro = max(st.max_rel_fro, relf)
         st.max_lse = max(st.max_lse, lerr)
         st.calls += 1
-        assert err <= TOL[dt], f"O max-abs {err:.3e} > {TOL[dt]}"
+        assert err <= tol, f"O max-abs {err:.3e} > {tol:.3e}"
         assert relf <= RELF_TOL[dt], f"O rel-Frobenius {relf:.3e} > {RELF_TOL[dt]}"
         assert lerr <= LSE_TOL[dt], f"LSE max-abs {lerr:.3e} > {LSE_TOL[dt]}"
         if O_ctrl is not None:

@@ -164,8 +164,9 @@ def test_rollout_bookkeeping_matches_oracle(rule):
                 ff.ff_render_attend(hc.ctx, i, k, FAKE, FAKE, FAKE, FAKE, L=hc.L)
                 ro.render_attend(i, k, None, z, z, compute=False)
                 # the key table handed to the kernel points at the right blocks
-                offs, ntoks, lk, _ = hc.last_segments()
+                offs, ntoks, lk, ntiles = hc.last_segments()
                 assert ntoks == ntok and lk == sum(ntok)
+                assert ntiles == sum((n + 63) // 64 for n in ntok)      # sources padded to 64-key tiles
                 for (s, idx), off in zip(src, offs):
                     if s == "anchor":
                         assert off == idx * anchor_block
