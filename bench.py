@@ -44,6 +44,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload):
+    """HBM bytes per attention dispatch from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"attn_{workload}_traffic.md")
+    src = os.path.join(ROOT, "chunked_kv_cache_amd", "csrc", "hip", "ff_kernels.hip")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", "-", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if fields.get("kernel_source_sha256_16") != h or "traffic_bytes_per_dispatch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_dispatch"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,7 +210,8 @@ def main():
         "publish_gbps": round(pub_gbps, 1),
         "publish_pct_hbm": round(100 * pub_gbps / PEAK_HBM_GBPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
