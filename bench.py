@@ -219,8 +219,10 @@ def main():
 
 
 def cpu_baseline(ctx, host_qkv, chunk, T, nh, d, n_heads_sample, n_latents):
-    """The float64 oracle's attention on a bounded sample of the same step:
-    all queries of the first `n_heads_sample` heads against the full key set."""
+    """The float64 oracle on a bounded sample of the same workload: its whole
+    renderer call (order checks, gather of the key sources, attention, Tail_H
+    publish) for two consecutive steady-state chunks (`chunk`, `chunk`+1, both
+    20 key latents at 480p), on the first `n_heads_sample` heads."""
     import numpy as np
     import oracle as orc
     import synthetic as syn
@@ -230,25 +232,29 @@ def cpu_baseline(ctx, host_qkv, chunk, T, nh, d, n_heads_sample, n_latents):
                       default=len(os.sched_getaffinity(0)))
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=nh, head_dim=d, n_latents=n_latents, n_stages=1)
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=n_heads_sample, head_dim=d, n_latents=n_latents, n_stages=1)
     ro = orc.Rollout(cfg)
     hs = slice(0, n_heads_sample)
-    for a in orc.gamma(cfg, chunk):
+    f64 = lambda x: syn.as_f64(x, "bf16")[:, hs]
+    for a in sorted(set(orc.gamma(cfg, chunk)) | set(orc.gamma(cfg, chunk + 1))):
         K, V = syn.anchor_kv(T=T, n_heads=nh, head_dim=d, anchors=[a])
-        ro.anchors[a] = (syn.as_f64(K, "bf16")[:, hs], syn.as_f64(V, "bf16")[:, hs])
+        ro.anchors[a] = (f64(K), f64(V))
     for i in range(max(0, chunk - cfg.history), chunk):
         _, kk, vv = syn.chunk_qkv(T=T, n_heads=nh, head_dim=d, chunk=i, stage=0)
-        ro.banks[0].append((i, syn.as_f64(kk, "bf16")[:, hs], syn.as_f64(vv, "bf16")[:, hs]))
+        ro.banks[0].append((i, f64(kk), f64(vv)))
     ro.next_chunk[0] = chunk
-    q, kk, vv = (syn.as_f64(x, "bf16")[:, hs] for x in host_qkv)
-    Kc, Vc = ro.gather_keys(chunk, 0, kk, vv)
+    calls = [(chunk, [f64(x) for x in host_qkv]),
+             (chunk + 1, [f64(x) for x in syn.chunk_qkv(T=T, n_heads=nh, head_dim=d, chunk=chunk + 1, stage=0)])]
+    flops = 0.0
     t0 = time.perf_counter()
-    orc.attention(q, Kc, Vc, cfg.scale)
+    for i, (q, kk, vv) in calls:
+        ro.render_attend(i, 0, q, kk, vv)
     dt = time.perf_counter() - t0
-    flops = 4.0 * q.shape[0] * Kc.shape[0] * d * n_heads_sample
+    for i in (chunk, chunk + 1):
+        flops += 4.0 * 3 * T * T * orc.key_latents(cfg, i, cfg.history) * d * n_heads_sample
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 oracle attention of chunk {chunk}, {n_heads_sample} of {nh} heads, all "
-                      f"{q.shape[0]} queries x {Kc.shape[0]} keys ({flops / 1e9:.0f} GFLOP in {dt:.1f} s)"}
+            "sample": f"float64 oracle renderer calls for chunks {chunk} and {chunk + 1} (stage 0, 20 key "
+                      f"latents each), {n_heads_sample} of {nh} heads: {flops / 1e9:.0f} GFLOP in {dt:.1f} s"}
 
 
 if __name__ == "__main__":
