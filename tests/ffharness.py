@@ -79,7 +79,8 @@ class Stats:
 class Pair:
     """GPU context + oracle rollout driven in lockstep."""
 
-    def __init__(self, case: Case, poison_workspace: bool = True, oracle_compute: bool = True):
+    def __init__(self, case: Case, poison_workspace: bool = True, oracle_compute: bool = True,
+                 device_bank_check: bool = False):
         import torch
         self.case = case
         self.cfg = case.cfg
@@ -95,6 +96,10 @@ class Pair:
         self.vmax = {}                       # max |V| per key source, for the rounding bound
         self.stats = Stats()
         self.oracle_compute = oracle_compute
+        # full-size cases: compare bank bytes on the device against the exact
+        # input tensors (kept while they can still be in a bank)
+        self.device_bank_check = device_bank_check
+        self.dev_inputs = {}
 
     @property
     def ctx(self):
@@ -143,7 +148,11 @@ class Pair:
             vkeys = max(self.vmax[("anchor", x)] if kind == "anchor" else self.vmax[("history", (x, k))]
                         for kind, x in self.ro.key_sources(i, k))
             O_ref, L_ref = self.ro.render_attend(i, k, q64, k64, v64, rows=rows, compute=self.oracle_compute)
-            self.inputs[(i, k)] = (h[1], h[2])
+            if self.device_bank_check:
+                self.dev_inputs[(i, k)] = (dev[j][1], dev[j][2])
+                self.dev_inputs.pop((i - c.H - 1, k), None)
+            else:
+                self.inputs[(i, k)] = (h[1], h[2])
             if self.oracle_compute:
                 O = from_device_f64(outs[j])
                 L = lses[j].cpu().numpy().astype(np.float64)
@@ -203,6 +212,14 @@ class Pair:
         if n == 0:
             return
         torch.cuda.synchronize()
+        if self.device_bank_check:
+            L = 3 * c.T
+            for j, cid in enumerate(ids):
+                kin, vin = self.dev_inputs[(cid, k)]
+                assert torch.equal(Ko[j * L:(j + 1) * L].view(torch.int16), kin.view(torch.int16))
+                assert torch.equal(Vo[j * L:(j + 1) * L].view(torch.int16), vin.view(torch.int16))
+            self.stats.bank_checks += 1
+            return
         kbits = np.concatenate([self.inputs[(i, k)][0] for i in ids])
         vbits = np.concatenate([self.inputs[(i, k)][1] for i in ids])
         view = (lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)) if c.dtype == "bf16" else \

@@ -134,3 +134,44 @@ def test_480p_steps_sampled_rows():
               f"control>={pr.stats.min_control_ratio:.1f}x")
     finally:
         pr.close()
+
+
+def test_480p_rollout_grouped_full_size():
+    """One-layer 81-latent rollout at the 480p shape (T=1560, 12 heads, d=128):
+    9 anchors in 3 planner blocks, then the 30 anti-diagonals of 27 chunks x 4
+    stages as grouped launches (108 calls).  Every call: O and LSE on 16
+    sampled query rows against the oracle; every stage bank's ids and bytes
+    after every call."""
+    import sys
+    case = Case(T=1560, nh=12, d=128, S=4)
+    rows = np.sort(np.random.default_rng(11).choice(3 * 1560, size=16, replace=False))
+    pr = Pair(case, device_bank_check=True)
+    try:
+        pr.publish_anchors()
+        for t, diag in enumerate(orc.schedule(case.cfg)):
+            pr.step(diag, grouped=True, rows=rows, control=(t == 12))
+            print(f"  diagonal {t}: {len(diag)} pairs ok", flush=True, file=sys.stderr)
+        assert pr.stats.calls == 108 and pr.stats.bank_checks == 108
+        print(f"480p rollout grouped: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
+              f"control>={pr.stats.min_control_ratio:.1f}x")
+    finally:
+        pr.close()
+
+
+def test_720p_step_sampled_rows():
+    """720p / 14B shape (T=3600, 40 heads, d=128): chunks 0..5 at stage 0, chunk 5
+    is the 20-latent step (10800 queries x 72000 keys); 8 sampled query rows
+    per call against the oracle, banks exact."""
+    import sys
+    case = Case(T=3600, nh=40, d=128, S=1)
+    rows = np.sort(np.random.default_rng(5).choice(3 * 3600, size=8, replace=False))
+    pr = Pair(case, device_bank_check=True)
+    try:
+        pr.publish_anchors()
+        for i in range(6):
+            pr.step([(i, 0)], grouped=False, rows=rows, control=(i == 5))
+            print(f"  720p chunk {i} ok", flush=True, file=sys.stderr)
+        print(f"720p chunks 0..5: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
+              f"control>={pr.stats.min_control_ratio:.1f}x")
+    finally:
+        pr.close()
