@@ -58,15 +58,21 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 // arrays.  The LDS layouts are XOR-swizzled for conflict-free 16-byte reads;
 // the swizzle is applied by choosing which global chunk each lane fetches.
 // --------------------------------------------------------------------------
-constexpr int kWaves = 8;          // waves per work item: 2 per SIMD, 32 queries each
+// Waves per work item.  Wave w owns 256 / NW query rows as blocks of 32; every
+// K or V^T operand read from LDS feeds one MFMA per block.  Eight waves (two
+// per SIMD, 32 rows each) let one wave's LDS reads and softmax hide behind
+// the other's MFMAs; four waves of 64 rows halve the LDS reads but leave each
+// SIMD a single instruction stream, and measure slower.
+constexpr int kAttnWaves = 8;
 
-template <int D>
+template <int D, int NW>
 struct TileCfg {
   static constexpr int kKBytes = kBlockN * D * 2;     // K tile [64][D]
   static constexpr int kVBytes = D * kBlockN * 2;     // V^T tile [D][64]
   static constexpr int kBufBytes = kKBytes + kVBytes;
-  static constexpr int kKBlocks = kKBytes / 1024 / kWaves;   // 1 KB DMA blocks per wave
-  static constexpr int kVBlocks = kVBytes / 1024 / kWaves;
+  static constexpr int kKBlocks = kKBytes / 1024 / NW;   // 1 KB DMA blocks per wave
+  static constexpr int kVBlocks = kVBytes / 1024 / NW;
+  static constexpr int kDmaPerTile = kKBlocks + kVBlocks;
   static constexpr int kRowsPerKBlock = 1024 / (2 * D);
   static constexpr int kChunksPerRow = D / 8;
 };
@@ -85,17 +91,29 @@ __device__ __forceinline__ int krow_swz(int r) {
 __device__ __forceinline__ int vrow_swz(int dd) { return (dd & 7) ^ ((dd >> 3) & 1); }
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(1))) void glb_void;
 
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds((glb_void*)(g), (lds_void*)(l), 16, 0, 0);
+// Raw buffer resource over [base, base + bytes): loads at or past the end
+// return zeros.  Word 3 selects the 32-bit data format that untyped gfx9
+// buffer loads need.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset voff into LDS: a wave writes 1 KB,
+// lane i to bytes 16i..16i+15 of dst.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint8_t* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, 0, 0, 0);
 }
 
 // Wait until this wave's outstanding global->LDS copies have landed
-// (vmcnt(0)), or all but the newest N (vmcnt(N), N < 16).
+// (vmcnt(0)), or all but the newest N (vmcnt(N); the field's low 4 bits sit
+// in bits 3:0 of the immediate and its high 2 bits in bits 15:14).
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 template <int N>
-__device__ __forceinline__ void wait_dma_but() { __builtin_amdgcn_s_waitcnt(0x0F70 | N); }
+__device__ __forceinline__ void wait_dma_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ int xcd_remap(int b, int nb) {
   // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
@@ -105,16 +123,49 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
-// Key-source cursor of one wave (all fields wave-uniform).
-template <int D>
+// Per-lane constants of the tile copies and operand reads (set once).
+template <int D, int NW>
+struct LaneConst {
+  uint32_t kdma[TileCfg<D, NW>::kKBlocks];   // K copy j: byte offset from the tile's first key row
+  uint32_t kread[D / 16];                    // K operand of k-step ks, half 0: LDS byte offset
+  uint32_t vread[2][2];                      // V^T operand (half, j), rows 0..31: LDS byte offset
+};
+
+template <int D, int NW>
+__device__ __forceinline__ void lane_const(LaneConst<D, NW>& lc, int w, int lane) {
+  using Cfg = TileCfg<D, NW>;
+  constexpr int CPR = Cfg::kChunksPerRow;
+#pragma unroll
+  for (int j = 0; j < Cfg::kKBlocks; ++j) {
+    const int r = (w * Cfg::kKBlocks + j) * Cfg::kRowsPerKBlock + lane / CPR;
+    lc.kdma[j] = uint32_t(r * D * 2 + (((lane % CPR) ^ krow_swz<D>(r)) << 4));
+  }
+  const int l32 = lane & 31, hl = lane >> 5;
+  // Row of the K tile this lane feeds as A operand (bits 2 and 3 swapped).
+  const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    lc.kread[ks] = uint32_t(prow * D * 2 + (((2 * ks + hl) ^ krow_swz<D>(prow)) << 4));
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      lc.vread[half][j] = uint32_t(l32 * kBlockN * 2 + (((4 * half + 2 * j + hl) ^ vrow_swz(l32)) << 4));
+}
+
+// Key-source cursor of one wave (pointers and counts wave-uniform).
+template <int D, int NW>
 struct SrcCursor {
   const __bf16* k;      // K rows of this head, key 0 of the source
   const __bf16* v;      // V^T of this head, [D][n]
   int n, t0, t1, s;
+  uint32_t vdma[TileCfg<D, NW>::kVBlocks];   // V^T copy j: lane byte offset from the tile's first key
 };
 
-template <int D>
-__device__ __forceinline__ void cursor_set(SrcCursor<D>& c, const SegTable& t, int s, int h, int nh) {
+template <int D, int NW>
+__device__ __forceinline__ void cursor_set(SrcCursor<D, NW>& c, const SegTable& t, int s, int h, int nh, int w,
+                                           int lane) {
+  using Cfg = TileCfg<D, NW>;
   c.s = s;
   c.n = t.n[s];
   c.t0 = t.tile_start[s];
@@ -122,35 +173,30 @@ __device__ __forceinline__ void cursor_set(SrcCursor<D>& c, const SegTable& t, i
   const __bf16* base = static_cast<const __bf16*>(t.base[s]);
   c.k = base + int64_t(h) * c.n * D;
   c.v = base + int64_t(nh) * c.n * D + int64_t(h) * D * c.n;
+#pragma unroll
+  for (int j = 0; j < Cfg::kVBlocks; ++j) {
+    const int dd = (w * Cfg::kVBlocks + j) * 8 + lane / 8;
+    c.vdma[j] = uint32_t(dd * c.n * 2 + (((lane & 7) ^ vrow_swz(dd)) << 4));
+  }
 }
 
-// Issue the copies of tile t (inside the cursor's source) into buf.
-// Returns the number of valid keys of the tile (64 except a source's last).
-template <int D>
-__device__ __forceinline__ int issue_tile(const SrcCursor<D>& c, int t, uint8_t* buf, int w, int lane) {
-  constexpr int CPR = TileCfg<D>::kChunksPerRow;
+// Issue the copies of tile t (inside the cursor's source) into kbuf / vbuf.
+// Each copy reads through a buffer resource that ends with the head's data:
+// K rows past the source's last key read as zeros, and V^T chunks past it
+// read the next row's first keys (or zeros after the last row); those keys
+// are masked, so their p is exactly 0.  Returns the tile's valid key count.
+template <int D, int NW>
+__device__ __forceinline__ int issue_tile(const SrcCursor<D, NW>& c, const LaneConst<D, NW>& lc, int t,
+                                          uint8_t* kbuf, uint8_t* vbuf, int w) {
+  using Cfg = TileCfg<D, NW>;
   const int o = (t - c.t0) * kBlockN;
-  const int valid = min(kBlockN, c.n - o);
-  const __bf16* kt = c.k + int64_t(o) * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(c.k + int64_t(o) * D, uint32_t(c.n - o) * D * 2);
 #pragma unroll
-  for (int j = 0; j < TileCfg<D>::kKBlocks; ++j) {
-    const int b = w * TileCfg<D>::kKBlocks + j;
-    int r = b * TileCfg<D>::kRowsPerKBlock + lane / CPR;
-    const int ch = (lane % CPR) ^ krow_swz<D>(r);
-    r = r < valid ? r : 0;                           // rows past the source: any valid row
-    dma16(kt + r * D + ch * 8, buf + b * 1024);
-  }
-  const __bf16* vt = c.v + o;
-  uint8_t* vbuf = buf + TileCfg<D>::kKBytes;
+  for (int j = 0; j < Cfg::kKBlocks; ++j) dma16(rk, lc.kdma[j], kbuf + (w * Cfg::kKBlocks + j) * 1024);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(c.v + o, uint32_t(D * c.n - o) * 2);
 #pragma unroll
-  for (int j = 0; j < TileCfg<D>::kVBlocks; ++j) {
-    const int b = w * TileCfg<D>::kVBlocks + j;
-    const int dd = b * 8 + lane / 8;
-    int ch = (lane & 7) ^ vrow_swz(dd);
-    ch = ch * 8 < valid ? ch : 0;
-    dma16(vt + int64_t(dd) * c.n + ch * 8, vbuf + b * 1024);
-  }
-  return valid;
+  for (int j = 0; j < Cfg::kVBlocks; ++j) dma16(rv, c.vdma[j], vbuf + (w * Cfg::kVBlocks + j) * 1024);
+  return min(kBlockN, c.n - o);
 }
 
 // --------------------------------------------------------------------------
@@ -176,35 +222,42 @@ struct WaveState {
   float m, l;                // running max (base 2) and per-lane partial sum
 };
 
-// S^T for one 32-key half (keys 32*half .. +31 of the tile in buf).
-template <int D>
-__device__ __forceinline__ void qk_half(const uint8_t* buf, int half, const bf16x8 (&qreg)[D / 16], f32x16& s,
-                                        int hl, int prow) {
-  const int row = 32 * half + prow;
-  const uint8_t* kbase = buf + row * (D * 2);
-  const int sw = krow_swz<D>(row);
+// S^T for one 32-key half (keys 32*half .. +31 of the K tile kbuf), for the
+// wave's R blocks of 32 queries: each K operand read feeds R MFMAs.
+template <int D, int NW, int R>
+__device__ __forceinline__ void qk_half(const uint8_t* kbuf, int half, const LaneConst<D, NW>& lc,
+                                        const bf16x8 (&qreg)[R][D / 16], f32x16 (&s)[R]) {
   const f32x16 zero = {};
-  s = zero;
+#pragma unroll
+  for (int b = 0; b < R; ++b) s[b] = zero;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const int ch = 2 * ks + hl;
-    const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(kbase + ((ch ^ sw) << 4)));
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[ks], s, 0, 0, 0);
+    const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(kbuf + lc.kread[ks] + half * 32 * D * 2));
+#pragma unroll
+    for (int b = 0; b < R; ++b) s[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qreg[b][ks], s[b], 0, 0, 0);
   }
 }
 
-// Register r of this lane holds key 16*(r/8) + 8*hl + r%8 of the half.
+// Register r of this lane holds key 16*(r/8) + 8*hl + r%8 of the half; keys
+// at or past `limit` are masked (the per-register offsets are constants, so
+// only the lane's threshold lives in a register).
 __device__ __forceinline__ void mask_half(f32x16& s, int limit, int hl) {
+  const int lim = limit - 8 * hl;
 #pragma unroll
   for (int r = 0; r < 16; ++r)
-    if (16 * (r >> 3) + 8 * hl + (r & 7) >= limit) s[r] = -INFINITY;
+    if (16 * (r >> 3) + (r & 7) >= lim) s[r] = -INFINITY;
 }
 
+// Two interleaved chains of 3-input maxima (8 VALU ops for 16 values).
 __device__ __forceinline__ float rowmax_half(const f32x16& s) {
-  float a = fmaxf(s[0], s[1]);
-#pragma unroll
-  for (int r = 2; r < 16; r += 2) a = fmaxf(a, fmaxf(s[r], s[r + 1]));
-  return half_swap_max(a);
+  float a = fmaxf(s[0], fmaxf(s[1], s[2]));
+  float b = fmaxf(s[3], fmaxf(s[4], s[5]));
+  a = fmaxf(a, fmaxf(s[6], s[7]));
+  b = fmaxf(b, fmaxf(s[8], s[9]));
+  a = fmaxf(a, fmaxf(s[10], s[11]));
+  b = fmaxf(b, fmaxf(s[12], s[13]));
+  a = fmaxf(a, fmaxf(s[14], s[15]));
+  return half_swap_max(fmaxf(a, b));
 }
 
 // Raise the running max when a half's max exceeds it by more than the
@@ -240,32 +293,39 @@ __device__ __forceinline__ void softmax_p(const f32x16& s, float c, WaveState<D>
   st.l += lsum;
 }
 
-// O^T += V^T P^T for one 32-key half.
-template <int D>
-__device__ __forceinline__ void pv_half(const uint8_t* buf, int half, const bf16x8 (&pb)[2], WaveState<D>& st,
-                                        int l32, int hl) {
-  const uint8_t* vbase = buf + TileCfg<D>::kKBytes;
+// O^T += V^T P^T for one 32-key half of the V^T tile vbuf; each operand read
+// feeds R MFMAs.
+template <int D, int NW, int R>
+__device__ __forceinline__ void pv_half(const uint8_t* vbuf, int half, const LaneConst<D, NW>& lc,
+                                        const bf16x8 (&pb)[R][2], WaveState<D> (&st)[R]) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int ch = 4 * half + 2 * j + hl;
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const int dd = 32 * db + l32;
-      const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbase + dd * (kBlockN * 2) + ((ch ^ vrow_swz(dd)) << 4)));
-      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[j], st.o[db], 0, 0, 0);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbuf + lc.vread[half][j] + db * 32 * kBlockN * 2));
+#pragma unroll
+      for (int b = 0; b < R; ++b)
+        st[b].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[b][j], st[b].o[db], 0, 0, 0);
     }
-  }
 }
+
+// The four K and V^T tile buffers of a workgroup.
+struct LdsBufs {
+  uint8_t* k[4];
+  uint8_t* v[4];
+};
 
 // One piece of work: item (head h, query tile qt) over key tiles [t_begin,
 // t_end).  A whole item writes O and LSE; a piece writes its unnormalised O,
-// running max and sum to `slot` for the merge kernel.
-template <int D>
+// running max and sum to `slot` for the merge kernel.  Wave w owns query rows
+// 32*R*w .. 32*R*w + 32*R - 1 of the tile, as R blocks of 32.
+template <int D, int NW>
 __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& P, int item, int t_begin, int t_end,
-                                         float* slot, uint8_t* lds0, uint8_t* lds1, uint8_t* lds2, uint8_t* lds3) {
+                                         float* slot, const LdsBufs& lb) {
   constexpr int KS = D / 16;       // MFMA k-steps over head_dim
   constexpr int DB = D / 32;       // 32-row blocks of O^T
-  constexpr int kDmaPerTile = TileCfg<D>::kKBlocks + TileCfg<D>::kVBlocks;   // per wave
+  constexpr int R = kBlockM / NW / 32;
+  constexpr int kDma = TileCfg<D, NW>::kDmaPerTile;   // per wave
   const int nh = a.nh, lq = a.lq;
   const int qt = item % a.n_qtiles;
   const int h = item / a.n_qtiles;
@@ -273,126 +333,145 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int row = w * 32 + l32;                  // query row within the tile
-  const int q = qt * kBlockM + row;
-  const bool q_ok = q < lq;
+  const int row0 = w * 32 * R + l32;             // query row of block 0 within the tile
 
-  // Q^T as the B operand: lane holds Q[q][16*ks + 8*hl .. +7].
-  bf16x8 qreg[KS];
-  {
-    const __bf16* qp = static_cast<const __bf16*>(P.q) + (int64_t(q_ok ? q : 0) * nh + h) * D + 8 * hl;
+  // Q^T as the B operand: lane holds Q[q][16*ks + 8*hl .. +7] of its R rows.
+  bf16x8 qreg[R][KS];
+#pragma unroll
+  for (int b = 0; b < R; ++b) {
+    const int q = qt * kBlockM + row0 + 32 * b;
+    const bool ok = q < lq;
+    const __bf16* qp = static_cast<const __bf16*>(P.q) + (int64_t(ok ? q : 0) * nh + h) * D + 8 * hl;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 v = ld16(qp + 16 * ks);
-      if (!q_ok) v = u32x4{0u, 0u, 0u, 0u};
-      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+      if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+      qreg[b][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
   const float c = a.scale * kLog2e;
-  // Row of the K tile this lane feeds as A operand (bits 2 and 3 swapped).
-  const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  LaneConst<D, NW> lc;
+  lane_const<D, NW>(lc, w, lane);
 
-  WaveState<D> st;
+  WaveState<D> st[R];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int b = 0; b < R; ++b) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) st.o[db][r] = 0.f;
-  st.m = -INFINITY;
-  st.l = 0.f;
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[b].o[db][r] = 0.f;
+    st[b].m = -INFINITY;
+    st[b].l = 0.f;
+  }
 
-  SrcCursor<D> cur;
+  SrcCursor<D, NW> cur;
   {
     int s = 0;
     while (s + 1 < P.seg.nseg && t_begin >= P.seg.tile_start[s + 1]) ++s;
-    cursor_set<D>(cur, P.seg, s, h, nh);
+    cursor_set<D, NW>(cur, P.seg, s, h, nh, w, lane);
   }
-  auto issue = [&](int t, uint8_t* buf) -> int {
-    if (t >= cur.t1) cursor_set<D>(cur, P.seg, cur.s + 1, h, nh);
-    return issue_tile<D>(cur, t, buf, w, lane);
+  auto issue = [&](int t, int i) -> int {
+    if (t >= cur.t1) cursor_set<D, NW>(cur, P.seg, cur.s + 1, h, nh, w, lane);
+    return issue_tile<D, NW>(cur, lc, t, lb.k[i], lb.v[i], w);
+  };
+  // Scores of a half: mask keys past the source end, then apply the max.
+  auto finish_scores = [&](f32x16 (&s)[R], int limit) {
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      if (limit < 32) mask_half(s[b], limit, hl);
+      rescale<D>(rowmax_half(s[b]), c, st[b]);
+    }
+  };
+  auto softmax = [&](const f32x16 (&s)[R], bf16x8 (&pb)[R][2]) {
+#pragma unroll
+    for (int b = 0; b < R; ++b) softmax_p<D>(s[b], c, st[b], pb[b]);
   };
 
-  f32x16 sa, sb;         // scores of the half awaiting softmax / being computed
-  bf16x8 pb[2];
+  f32x16 sa[R], sb[R];   // scores of the half awaiting softmax / being computed
+  bf16x8 pb[R][2];
   int valid[4];
   __syncthreads();       // the previous piece's reads of the buffers are done
-  valid[0] = issue(t_begin, lds0);
-  if (t_begin + 1 < t_end) valid[1] = issue(t_begin + 1, lds1);
-  if (t_begin + 2 < t_end) valid[2] = issue(t_begin + 2, lds2);
-  if (t_begin + 2 < t_end) wait_dma_but<2 * kDmaPerTile>();
-  else if (t_begin + 1 < t_end) wait_dma_but<kDmaPerTile>();
+  valid[0] = issue(t_begin, 0);
+  if (t_begin + 1 < t_end) valid[1] = issue(t_begin + 1, 1);
+  if (t_begin + 2 < t_end) valid[2] = issue(t_begin + 2, 2);
+  if (t_begin + 2 < t_end) wait_dma_but<2 * kDma>();
+  else if (t_begin + 1 < t_end) wait_dma_but<kDma>();
   else wait_dma();
   __syncthreads();
-  qk_half<D>(lds0, 0, qreg, sa, hl, prow);
-  if (valid[0] < 32) mask_half(sa, valid[0], hl);
-  rescale<D>(rowmax_half(sa), c, st);
+  qk_half<D, NW, R>(lb.k[0], 0, lc, qreg, sa);
+  finish_scores(sa, valid[0]);
 
-  // Tile t is in B (landed); B1 holds tile t+1 and B2 tile t+2 (both may still
-  // be landing); B3 is free for tile t+3.  Copies run two tiles ahead.
+  // Tile t is in buffer i (landed); buffer i+1 holds tile t+1 and i+2 tile
+  // t+2 (both may still be landing); buffer i+3 is free for tile t+3 (indices
+  // mod 4).  Copies run two tiles ahead.
   // Invariant at entry: sa = masked scores of half 0 of tile t, max applied.
-  auto tile = [&](const uint8_t* B, const uint8_t* B1, uint8_t* B3, int t, int v0, int v1, int v3) {
+  auto tile = [&](int t, int i) {
+    const int i1 = (i + 1) & 3, i3 = (i + 3) & 3;
     // half 0: S^T(half 1) and softmax(half 0) interleave; then PV(half 0)
-    qk_half<D>(B, 1, qreg, sb, hl, prow);
-    softmax_p<D>(sa, c, st, pb);
-    pv_half<D>(B, 0, pb, st, l32, hl);
-    if (valid[v0] < kBlockN) mask_half(sb, valid[v0] - 32, hl);
-    rescale<D>(rowmax_half(sb), c, st);
+    qk_half<D, NW, R>(lb.k[i], 1, lc, qreg, sb);
+    softmax(sa, pb);
+    pv_half<D, NW, R>(lb.v[i], 0, lc, pb, st);
+    finish_scores(sb, valid[i] - 32);
     // half 1: S^T(tile t+1, half 0) and softmax(half 1); then PV(half 1).
-    // On the last tile the S^T of B1 is computed on stale data and dropped.
+    // On the last tile the S^T of buffer i+1 is computed on stale data and dropped.
     const bool more = t + 1 < t_end;
     if (more) {
-      if (t + 2 < t_end) wait_dma_but<kDmaPerTile>();   // tile t+1 landed, t+2 may fly
+      if (t + 2 < t_end) wait_dma_but<kDma>();   // tile t+1 landed, t+2 may fly
       else wait_dma();
       __syncthreads();
-      if (t + 3 < t_end) valid[v3] = issue(t + 3, B3);
+      if (t + 3 < t_end) valid[i3] = issue(t + 3, i3);
     }
-    qk_half<D>(B1, 0, qreg, sa, hl, prow);
-    softmax_p<D>(sb, c, st, pb);
-    pv_half<D>(B, 1, pb, st, l32, hl);
-    if (more) {
-      if (valid[v1] < 32) mask_half(sa, valid[v1], hl);
-      rescale<D>(rowmax_half(sa), c, st);
-    }
+    qk_half<D, NW, R>(lb.k[i1], 0, lc, qreg, sa);
+    softmax(sb, pb);
+    pv_half<D, NW, R>(lb.v[i], 1, lc, pb, st);
+    if (more) finish_scores(sa, valid[i1]);
   };
 
   for (int t = t_begin; t < t_end; t += 4) {
-    tile(lds0, lds1, lds3, t, 0, 1, 3);
+    tile(t, 0);
     if (t + 1 >= t_end) break;
-    tile(lds1, lds2, lds0, t + 1, 1, 2, 0);
+    tile(t + 1, 1);
     if (t + 2 >= t_end) break;
-    tile(lds2, lds3, lds1, t + 2, 2, 3, 1);
+    tile(t + 2, 2);
     if (t + 3 >= t_end) break;
-    tile(lds3, lds0, lds2, t + 3, 3, 0, 2);
+    tile(t + 3, 3);
   }
 
   // ---- epilogue
-  const float l_tot = half_swap_sum(st.l);
-  if (!q_ok) return;
-  if (!slot) {
-    const float inv = 1.0f / l_tot;
-    __bf16* op = static_cast<__bf16*>(P.o) + (int64_t(q) * nh + h) * D + 4 * hl;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int b = 0; b < R; ++b) {
+    const float l_tot = half_swap_sum(st[b].l);
+    const int row = row0 + 32 * b;
+    const int q = qt * kBlockM + row;
+    if (q >= lq) continue;
+    if (!slot) {
+      const float inv = 1.0f / l_tot;
+      __bf16* op = static_cast<__bf16*>(P.o) + (int64_t(q) * nh + h) * D + 4 * hl;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(st.o[db][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(st[b].o[db][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
+        }
+      if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (st[b].m + log2f(l_tot)) * kLn2;
+    } else {
+      float* op = slot + row * D + 4 * hl;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& o = st[b].o[db];
+          *reinterpret_cast<float4*>(op + 32 * db + 8 * g) =
+              make_float4(o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]);
+        }
+      if (hl == 0) {
+        slot[kBlockM * D + row] = st[b].m;
+        slot[kBlockM * D + kBlockM + row] = l_tot;
       }
-    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (st.m + log2f(l_tot)) * kLn2;
-  } else {
-    float* op = slot + row * D + 4 * hl;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float4 ov = make_float4(st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2], st.o[db][4 * g + 3]);
-        *reinterpret_cast<float4*>(op + 32 * db + 8 * g) = ov;
-      }
-    if (hl == 0) {
-      slot[kBlockM * D + row] = st.m;
-      slot[kBlockM * D + kBlockM + row] = l_tot;
     }
   }
 }
@@ -417,30 +496,51 @@ __host__ __device__ inline RemSplit rem_split(int n_items, int ntiles, int n_wg)
   return r;
 }
 
-template <int D>
-__global__ __launch_bounds__(kWaves * 64, 1) void attn_bf16_kernel(const AttnLaunch a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds0[TileCfg<D>::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds1[TileCfg<D>::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds2[TileCfg<D>::kBufBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds3[TileCfg<D>::kBufBytes];
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch a) {
+  // One array per tile buffer, so that the compiler sees the copies into one
+  // buffer and the operand reads of another as disjoint.
+  using Cfg = TileCfg<D, NW>;
+  __shared__ __attribute__((aligned(1024))) uint8_t k0[Cfg::kKBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k1[Cfg::kKBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k2[Cfg::kKBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t k3[Cfg::kKBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0[Cfg::kVBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v1[Cfg::kVBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v2[Cfg::kVBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t v3[Cfg::kVBytes];
+  const LdsBufs lb = {{k0, k1, k2, k3}, {v0, v1, v2, v3}};
   // Consecutive workgroup ids sit on one XCD (shared L2).
   const int g = xcd_remap(blockIdx.x, gridDim.x);
   for (int p = 0; p < a.n_pairs; ++p) {
     const PairLaunch& P = a.pair[p];
     const RemSplit rs = rem_split(P.n_items, P.ntiles, a.n_wg);
-    for (int r = 0; r < rs.full; ++r) run_item<D>(a, P, r * a.n_wg + g, 0, P.ntiles, nullptr, lds0, lds1, lds2, lds3);
-    if (rs.rem == 0) continue;
     const int base = rs.full * a.n_wg;
     const bool cut = rs.F < P.ntiles;
+    // Pieces of this workgroup: rs.full whole items, then its last-round share.
+    int n_last = 0, first_tail = 0;
     if (g < rs.rem) {
-      run_item<D>(a, P, base + g, 0, rs.F, cut ? P.part + int64_t(g) * 2 * a.slot_floats : nullptr, lds0, lds1,
-                  lds2, lds3);
+      n_last = 1;
     } else if (cut) {
-      const int j = g - rs.rem;
-      const int i_end = min(rs.rem, (j + 1) * rs.k);
-      for (int i = j * rs.k; i < i_end; ++i)
-        run_item<D>(a, P, base + i, rs.F, P.ntiles, P.part + (int64_t(i) * 2 + 1) * a.slot_floats, lds0, lds1, lds2,
-                    lds3);
+      first_tail = (g - rs.rem) * rs.k;
+      n_last = max(0, min(rs.rem, first_tail + rs.k) - first_tail);
+    }
+    for (int u = 0; u < rs.full + n_last; ++u) {
+      int item = u * a.n_wg + g, t_begin = 0, t_end = P.ntiles;
+      float* slot = nullptr;
+      if (u >= rs.full) {
+        if (g < rs.rem) {
+          item = base + g;
+          t_end = rs.F;
+          if (cut) slot = P.part + int64_t(g) * 2 * a.slot_floats;
+        } else {
+          const int i = first_tail + (u - rs.full);
+          item = base + i;
+          t_begin = rs.F;
+          slot = P.part + (int64_t(i) * 2 + 1) * a.slot_floats;
+        }
+      }
+      run_item<D, NW>(a, P, item, t_begin, t_end, slot, lb);
     }
   }
 }
@@ -740,8 +840,9 @@ int dev_launch_attention(const AttnLaunch& a, void* stream, Profiler* prof) {
   }
   {
     Timed tm(prof, kAttn, s);
-    if (a.d == 64) hipLaunchKernelGGL(attn_bf16_kernel<64>, dim3(a.n_wg), dim3(kWaves * 64), 0, s, a);
-    else hipLaunchKernelGGL(attn_bf16_kernel<128>, dim3(a.n_wg), dim3(kWaves * 64), 0, s, a);
+    const dim3 grid(a.n_wg), block(kAttnWaves * 64);
+    if (a.d == 64) hipLaunchKernelGGL((attn_bf16_kernel<64, kAttnWaves>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, kAttnWaves>), grid, block, 0, s, a);
   }
   if (launch_ok()) return FF_E_HIP;
   {
