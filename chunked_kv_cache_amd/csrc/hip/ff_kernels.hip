@@ -548,23 +548,29 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch 
 // --------------------------------------------------------------------------
 // Merge of the items cut in the last round: O = sum_j 2^(m_j - M) O_j /
 // sum_j 2^(m_j - M) l_j over the head piece (j = 0) and the tail piece (j = 1).
-// One block per cut item and call; D/4 consecutive threads share a query row,
-// each taking 4 head-dim values, so partial reads and O writes are coalesced.
+// One block per 32 query rows of a cut item and call; D/4 consecutive threads
+// share a query row, each taking 4 head-dim values, so partial reads and O
+// writes are coalesced.
 // --------------------------------------------------------------------------
+constexpr int kMergeRows = 32;   // query rows per merge block
+
 template <int D>
 __global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
   constexpr int TPR = D / 4;                     // threads per row
   constexpr int RPP = 256 / TPR;                 // rows per pass
   const PairLaunch& P = a.pair[blockIdx.y];
   const RemSplit rs = rem_split(P.n_items, P.ntiles, a.n_wg);
-  const int i = blockIdx.x;
+  const int i = blockIdx.x / (kBlockM / kMergeRows);
   if (i >= rs.rem || rs.F >= P.ntiles) return;
   const int item = rs.full * a.n_wg + i;
   const int qt = item % a.n_qtiles, h = item / a.n_qtiles;
   const float* s0 = P.part + int64_t(i) * 2 * a.slot_floats;
   const float* s1 = s0 + a.slot_floats;
   const int c4 = threadIdx.x % TPR;
-  for (int row = threadIdx.x / TPR; row < kBlockM; row += RPP) {
+  const int r0 = (blockIdx.x % (kBlockM / kMergeRows)) * kMergeRows + threadIdx.x / TPR;
+#pragma unroll
+  for (int pass = 0; pass < kMergeRows / RPP; ++pass) {
+    const int row = r0 + pass * RPP;
     const int q = qt * kBlockM + row;
     if (q >= a.lq) break;
     const float m0 = s0[kBlockM * D + row], m1 = s1[kBlockM * D + row];
@@ -853,7 +859,7 @@ int dev_launch_attention(const AttnLaunch& a, void* stream, Profiler* prof) {
       if (rs.F < a.pair[p].ntiles && rs.rem > max_rem) max_rem = rs.rem;
     }
     if (max_rem == 0) return 0;
-    dim3 grid(unsigned(max_rem), unsigned(a.n_pairs));
+    dim3 grid(unsigned(max_rem * (kBlockM / kMergeRows)), unsigned(a.n_pairs));
     if (a.d == 64) hipLaunchKernelGGL(merge_pieces_kernel<64>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(merge_pieces_kernel<128>, grid, dim3(256), 0, s, a);
   }
