@@ -376,12 +376,23 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     return issue_tile<D, NW>(cur, lc, t, lb.k[i], lb.v[i], w);
   };
   // Scores of a half: mask keys past the source end, then apply the max.
+  // Scores of a half: keys at or past `limit` masked, then the running max
+  // applied.  The row maxima of the unmasked scores come first, outside the
+  // (rarely taken) masking branch, so that they share a basic block with the
+  // MFMAs issued before them and can overlap them.
   auto finish_scores = [&](f32x16 (&s)[R], int limit) {
+    float mx[R];
 #pragma unroll
-    for (int b = 0; b < R; ++b) {
-      if (limit < 32) mask_half(s[b], limit, hl);
-      rescale<D>(rowmax_half(s[b]), c, st[b]);
+    for (int b = 0; b < R; ++b) mx[b] = rowmax_half(s[b]);
+    if (limit < 32) {
+#pragma unroll
+      for (int b = 0; b < R; ++b) {
+        mask_half(s[b], limit, hl);
+        mx[b] = rowmax_half(s[b]);
+      }
     }
+#pragma unroll
+    for (int b = 0; b < R; ++b) rescale<D>(mx[b], c, st[b]);
   };
   auto softmax = [&](const f32x16 (&s)[R], bf16x8 (&pb)[R][2]) {
 #pragma unroll
