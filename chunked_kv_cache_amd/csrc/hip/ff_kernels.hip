@@ -5,7 +5,7 @@
 //                 gathered from the anchor bank and the stage ring through the
 //                 call's key-source table into LDS (no concatenation copy).
 //  attn_f32<D>    plain fp32 path (one lane per query row and head).
-//  merge_pieces   LSE merge of the items the stream-K partition cut.
+//  merge_pieces   LSE merge of the items cut in the last scheduling round.
 //  publish        token-major K/V -> bank block (K head-major, V transposed).
 //  unpack         bank block -> token-major K/V (read-out of B_k).
 //
@@ -41,8 +41,8 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 // --------------------------------------------------------------------------
 // Segmented attention, bf16 in, fp32 accumulate.
 //
-// Work item = (pair, head, key split, 128-query tile); 4 waves x 32 queries;
-// 2 work items per CU.  Per 64-key tile:
+// Work item = (pair, head, 256-query tile), possibly cut into two key ranges
+// in the last round; one persistent workgroup per CU.  Per 64-key tile:
 //   S^T[key][q] = sum_d K[key][d] Q[q][d]     (A = K rows from LDS, B = Q regs)
 //   p = 2^(s*scale*log2e - m)                 (per query = per lane column)
 //   O^T[d][q] += sum_key V^T[d][key] P^T[key][q]  (A = V^T from LDS, B = P regs)
@@ -53,10 +53,11 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 // 0..7: P leaves the first MFMA already in B-operand order for the second,
 // and V^T rows are read as one contiguous 16-byte run per lane.
 //
-// K/V tiles go global -> LDS directly (global_load_lds_dwordx4, 1 KB per wave
-// instruction, lane i -> LDS bytes 16i..16i+15), double-buffered in two LDS
-// arrays.  The LDS layouts are XOR-swizzled for conflict-free 16-byte reads;
-// the swizzle is applied by choosing which global chunk each lane fetches.
+// K/V tiles go global -> LDS directly (buffer_load_dwordx4 ... lds, 1 KB per
+// wave instruction, lane i -> LDS bytes 16i..16i+15) into four K and four V^T
+// buffers, two tiles ahead of the math.  The LDS layouts are XOR-swizzled for
+// conflict-free 16-byte reads; the swizzle is applied by choosing which
+// global chunk each lane fetches.
 // --------------------------------------------------------------------------
 // Waves per work item.  Wave w owns 256 / NW query rows as blocks of 32; every
 // K or V^T operand read from LDS feeds one MFMA per block.  Eight waves (two
@@ -123,12 +124,23 @@ __device__ __forceinline__ int xcd_remap(int b, int nb) {
   return x * per + (x < rem ? x : rem) + idx;
 }
 
+// The V^T buffers sit past the 64 KB reach of a DS instruction's immediate
+// offset.  Their lane offsets carry a +64 KB bias that the optimiser cannot
+// see through, so that (buffer base - 64 KB + row block) folds into the
+// immediate and a V^T operand read costs no address arithmetic.  The address
+// is correct wherever the buffers land; only the folding depends on it.
+constexpr uint32_t kLdsBias = 65536;
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // Per-lane constants of the tile copies and operand reads (set once).
 template <int D, int NW>
 struct LaneConst {
   uint32_t kdma[TileCfg<D, NW>::kKBlocks];   // K copy j: byte offset from the tile's first key row
   uint32_t kread[D / 16];                    // K operand of k-step ks, half 0: LDS byte offset
-  uint32_t vread[2][2];                      // V^T operand (half, j), rows 0..31: LDS byte offset
+  uint32_t vread[2][2];                      // V^T operand (half, j), rows 0..31: LDS byte offset + kLdsBias
 };
 
 template <int D, int NW>
@@ -150,7 +162,8 @@ __device__ __forceinline__ void lane_const(LaneConst<D, NW>& lc, int w, int lane
   for (int half = 0; half < 2; ++half)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      lc.vread[half][j] = uint32_t(l32 * kBlockN * 2 + (((4 * half + 2 * j + hl) ^ vrow_swz(l32)) << 4));
+      lc.vread[half][j] = opaque(uint32_t(l32 * kBlockN * 2 + (((4 * half + 2 * j + hl) ^ vrow_swz(l32)) << 4)) +
+                                 kLdsBias);
 }
 
 // Key-source cursor of one wave (pointers and counts wave-uniform).
@@ -302,7 +315,8 @@ __device__ __forceinline__ void pv_half(const uint8_t* vbuf, int half, const Lan
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, ld16(vbuf + lc.vread[half][j] + db * 32 * kBlockN * 2));
+      const bf16x8 av = __builtin_bit_cast(
+          bf16x8, ld16(vbuf + (int32_t(lc.vread[half][j]) - int32_t(kLdsBias)) + db * 32 * kBlockN * 2));
 #pragma unroll
       for (int b = 0; b < R; ++b)
         st[b].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[b][j], st[b].o[db], 0, 0, 0);
