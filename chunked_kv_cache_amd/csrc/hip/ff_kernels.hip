@@ -389,7 +389,6 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     if (t >= cur.t1) cursor_set<D, NW>(cur, P.seg, cur.s + 1, h, nh, w, lane);
     return issue_tile<D, NW>(cur, lc, t, lb.k[i], lb.v[i], w);
   };
-  // Scores of a half: mask keys past the source end, then apply the max.
   // Scores of a half: keys at or past `limit` masked, then the running max
   // applied.  The row maxima of the unmasked scores come first, outside the
   // (rarely taken) masking branch, so that they share a basic block with the
