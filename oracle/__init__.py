@@ -2,5 +2,5 @@
 from .flashforward import (  # noqa: F401
     GAMMA_BRACKET, GAMMA_CENTER_LR, ContractError, FFConfig, Rollout, anchor_positions,
     ar_depth, attention, attention_rows, chunk_positions, gamma, history_ids_after,
-    is_legal_order, key_latents, n_anchors, n_chunks, planner_blocks, schedule,
+    is_legal_order, key_latents, n_anchors, n_chunks, planner_blocks, planner_key_blocks, schedule,
 )

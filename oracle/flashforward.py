@@ -34,6 +34,13 @@ Readings taken where the pages are silent (each also listed in the design doc):
   R7  Anchors are published once each, in planner blocks, and never evicted.
   R8  Call (i, k) also requires (i, k-1) to have run (the same-stage /
       previous-stage dependency of the wavefront schedule).
+  R11 Planner block b attends the clean anchor KV of the previous min(b, H_P)
+      planner blocks (H_P counts blocks: 6 x 3 + 3 = 21 = W_ctx) plus its own
+      in-flight K/V, with no mask inside; past W_ctx the oldest blocks are
+      dropped first.  The cache-extraction forward is the planner call whose
+      own K/V becomes the block's published anchor KV.
+  R12 Planner blocks run in order: block b needs blocks 0..b-1 published and
+      block b not yet published.
 
 Parity status per function is stated in each docstring.  gamma() and the W_ctx
 cap are "parity unpinned": no page prints the rule, so they are pinned only by
@@ -70,7 +77,7 @@ class FFConfig:
     anchor_stride: int = 10         # D (Delta)
     n_stages: int = 4               # S
     history: int = 5                # H
-    planner_history: int = 6        # H_P (planner side, not on this path)
+    planner_history: int = 6        # H_P, in planner blocks (reading R11)
     w_ctx: int = 21                 # context budget in latents
     gamma_rule: str = GAMMA_BRACKET
 
@@ -105,6 +112,22 @@ def planner_blocks(cfg: FFConfig) -> List[List[int]]:
     """
     ids = list(range(n_anchors(cfg)))
     return [ids[b:b + cfg.planner_block] for b in range(0, len(ids), cfg.planner_block)]
+
+
+def planner_key_blocks(cfg: FFConfig, b: int) -> List[int]:
+    """Planner blocks whose clean anchor KV planner block b attends, oldest first.
+
+    [S] how it differs: planner history H_P = 6; [S] training paragraph: a
+    planner block attends causally to the clean KV of earlier blocks (reading
+    R11: the last min(b, H_P) blocks, oldest dropped first past W_ctx).
+    """
+    blocks = planner_blocks(cfg)
+    if not 0 <= b < len(blocks):
+        raise ValueError("planner block out of range")
+    hist = list(range(max(0, b - cfg.planner_history), b))
+    while hist and sum(len(blocks[x]) for x in hist) + len(blocks[b]) > cfg.w_ctx:
+        hist = hist[1:]
+    return hist
 
 
 def n_chunks(cfg: FFConfig) -> int:
@@ -320,6 +343,59 @@ class Rollout:
         bank = self.banks[k] + [(i, np.array(K, copy=True), np.array(V, copy=True))]
         self.banks[k] = bank[-cfg.history:]
         self.next_chunk[k] = i + 1
+        return O, LSE
+
+    # -- the planner call -------------------------------------------------
+    def check_plan(self, b: int) -> None:
+        """Raise ContractError unless planner block b may run now (reading R12)."""
+        blocks = planner_blocks(self.cfg)
+        if not 0 <= b < len(blocks):
+            raise ContractError("planner block out of range")
+        for x in range(b):
+            for a in blocks[x]:
+                if a not in self.anchors:
+                    raise ContractError(f"planner block {x} (anchor {a}) not published")
+        for a in blocks[b]:
+            if a in self.anchors:
+                raise ContractError(f"anchor {a} of planner block {b} already published")
+
+    def plan_key_sources(self, b: int) -> List[Tuple[str, int]]:
+        """Ordered key sources of planner block b: earlier blocks' anchors, then its own latents."""
+        blocks = planner_blocks(self.cfg)
+        return ([("anchor", a) for x in planner_key_blocks(self.cfg, b) for a in blocks[x]] +
+                [("own", a) for a in blocks[b]])
+
+    def plan_attend(self, b: int, Q: np.ndarray, K: np.ndarray, V: np.ndarray, publish: bool = False,
+                    rows: Optional[Sequence[int]] = None, compute: bool = True):
+        """One planner call: block b attends its key sources; optionally publishes.
+
+        [S] how it differs: anchors are made B_P at a time and, once a block is
+        complete, one cache-extraction forward publishes its clean anchor KV;
+        [S] training paragraph: planner blocks attend causally to earlier
+        blocks' clean KV (readings R11, R12).  Q, K, V: [len(block)*T, nh, d].
+        With ``publish`` the call is the cache-extraction forward: K, V become
+        the block's anchors.  Returns (O, LSE) like render_attend.
+        """
+        self.check_plan(b)
+        cfg = self.cfg
+        blocks = planner_blocks(cfg)
+        O = LSE = None
+        if compute:
+            ks, vs = [], []
+            for kind, a in self.plan_key_sources(b):
+                if kind == "anchor":
+                    Ka, Va = self.anchors[a]
+                    ks.append(Ka)
+                    vs.append(Va)
+            ks.append(np.asarray(K))
+            vs.append(np.asarray(V))
+            Kc, Vc = np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+            if rows is None:
+                O, LSE = attention(Q, Kc, Vc, cfg.scale)
+            else:
+                O, LSE = attention_rows(Q, Kc, Vc, cfg.scale, rows)
+        if publish:
+            self.publish_anchors(blocks[b][0], K, V)
         return O, LSE
 
     def bank_tail(self, k: int):

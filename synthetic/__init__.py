@@ -11,9 +11,10 @@ Recipe (one stream per tensor, no stream is ever reused):
     -> standard_normal in float64 -> float32 -> (bf16 configs) bf16 by
        round-to-nearest-even of the float32 bit pattern.
 
-kind   : 0 = renderer chunk input, 1 = anchor (planner cache-extraction output)
-idx    : chunk id for kind 0, anchor id for kind 1
-stage  : denoising stage for kind 0, always 0 for kind 1
+kind   : 0 = renderer chunk input, 1 = anchor (planner cache-extraction output),
+         2 = planner block input during its denoising steps
+idx    : chunk id for kind 0, anchor id for kind 1, planner block for kind 2
+stage  : denoising stage for kind 0, always 0 for kind 1, step for kind 2
 tensor : 0 = Q, 1 = K, 2 = V
 
 Every tensor is token-major ``[tokens, n_heads, head_dim]``.
@@ -26,6 +27,7 @@ import numpy as np
 
 KIND_RENDER = 0
 KIND_ANCHOR = 1
+KIND_PLANNER = 2
 TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
 
 
@@ -88,3 +90,14 @@ def anchor_kv(*, T: int, n_heads: int, head_dim: int, anchors, seed: int = 0, la
         ks.append(normal_tensor((T, n_heads, head_dim), tensor=TENSOR_K, **kw))
         vs.append(normal_tensor((T, n_heads, head_dim), tensor=TENSOR_V, **kw))
     return np.concatenate(ks, axis=0), np.concatenate(vs, axis=0)
+
+
+def planner_qkv(*, T: int, n_heads: int, head_dim: int, block: int, step: int, n_latents: int, seed: int = 0,
+                layer: int = 0, dtype: str = "bf16", q_scale: float = 1.0):
+    """Q, K, V of planner block ``block`` at denoising step ``step``: each [n_latents*T, nh, d]."""
+    shape = (n_latents * T, n_heads, head_dim)
+    kw = dict(seed=seed, kind=KIND_PLANNER, layer=layer, idx=block, stage=step, dtype=dtype)
+    q = normal_tensor(shape, tensor=TENSOR_Q, scale=q_scale, **kw)
+    k = normal_tensor(shape, tensor=TENSOR_K, **kw)
+    v = normal_tensor(shape, tensor=TENSOR_V, **kw)
+    return q, k, v

@@ -28,6 +28,13 @@ MUTATIONS = {
     "anchor_grid_shifted": ("return list(range(0, cfg.n_latents, cfg.anchor_stride))",
                             "return list(range(cfg.anchor_stride, cfg.n_latents, cfg.anchor_stride))"),
     "softmax_sign": ("p = np.exp(s - m[:, None])", "p = np.exp(m[:, None] - s)"),
+    "planner_window_short": ("hist = list(range(max(0, b - cfg.planner_history), b))",
+                             "hist = list(range(max(0, b - cfg.planner_history + 1), b))"),
+    "planner_window_long": ("hist = list(range(max(0, b - cfg.planner_history), b))",
+                            "hist = list(range(max(0, b - cfg.planner_history - 1), b))"),
+    "planner_own_dropped": ("            ks.append(np.asarray(K))\n            vs.append(np.asarray(V))\n", ""),
+    "planner_no_order_check": ("        for x in range(b):\n            for a in blocks[x]:", "        for x in range(0):\n            for a in blocks[x]:"),
+    "planner_publish_shifted": ("self.publish_anchors(blocks[b][0], K, V)", "self.publish_anchors(blocks[b][-1], K, V)"),
 }
 
 

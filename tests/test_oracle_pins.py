@@ -359,3 +359,106 @@ def test_each_source_reaches_the_output(source):
     Q[:, 0] = 400.0 * target[0]           # score 50 against 0 for every other key
     O, _ = ro2.render_attend(i, 0, Q, Ks[i], Vs[i])
     np.testing.assert_allclose(O[:, 0, :], target[1], atol=1e-9)
+
+
+# --------------------------------------------------------------------------
+# Planner block attention (readings R11, R12)
+# --------------------------------------------------------------------------
+def _marker_planner_rollout(cfg, T, d=4):
+    """Anchors whose V rows all hold 1 + anchor id; keys all zero."""
+    ro = orc.Rollout(cfg)
+    return ro, (lambda a: (np.zeros((T, 1, d)), np.full((T, 1, d), 1.0 + a)))
+
+
+@pytest.mark.parametrize("n_latents,h_p,w_ctx", [(261, 6, 21), (261, 2, 21), (261, 6, 11), (81, 6, 21)])
+def test_planner_key_set_closed_form(golden, n_latents, h_p, w_ctx):
+    """Zero queries weight every key equally, so O = mean of the key values and
+    LSE = ln(number of keys): with one marker value per anchor and a separate
+    own value, both identify exactly which anchors block b reads."""
+    g = golden("worked_example_81.txt")
+    T, d = 2, 4
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=1, head_dim=d, n_latents=n_latents, planner_history=h_p,
+                       w_ctx=w_ctx)
+    assert cfg.planner_block == g["B_P"]
+    ro = orc.Rollout(cfg)
+    blocks = orc.planner_blocks(cfg)
+    for b, blk in enumerate(blocks):
+        n_own = len(blk) * T
+        Q = np.zeros((n_own, 1, d))
+        K = np.zeros((n_own, 1, d))
+        V = np.full((n_own, 1, d), 1000.0)
+        O, LSE = ro.plan_attend(b, Q, K, V)
+        # expected key set, written out: the H_P blocks before b, trimmed from
+        # the oldest while (their anchors + own latents) exceed W_ctx
+        first = max(0, b - h_p)
+        while first < b and 3 * (b - first) + len(blk) > w_ctx:
+            first += 1
+        anchors = [a for x in range(first, b) for a in range(3 * x, 3 * x + 3)]
+        n_keys = T * (len(anchors) + len(blk))
+        mean = (T * sum(1.0 + a for a in anchors) + n_own * 1000.0) / n_keys
+        np.testing.assert_allclose(O, mean, rtol=0, atol=1e-9)
+        np.testing.assert_allclose(LSE, math.log(n_keys), rtol=0, atol=1e-12)
+        # the cache-extraction call publishes the block with marker values
+        Kp = np.zeros((n_own, 1, d))
+        Vp = np.concatenate([np.full((T, 1, d), 1.0 + a) for a in blk])
+        ro.plan_attend(b, Q, Kp, Vp, publish=True, compute=False)
+        for a in blk:
+            np.testing.assert_array_equal(ro.anchors[a][1], np.full((T, 1, d), 1.0 + a))
+
+
+def test_planner_budget_at_pages_hyper_parameters(golden):
+    """H_P = 6 blocks of 3 plus the block itself is exactly W_ctx = 21 latents."""
+    g = golden("worked_example_81.txt")
+    assert g["H_P"] * g["B_P"] + g["B_P"] == g["W_ctx"]
+    cfg = orc.FFConfig(tokens_per_latent=2, n_heads=1, head_dim=4, n_latents=261)
+    assert orc.planner_key_blocks(cfg, 8) == [2, 3, 4, 5, 6, 7]
+    assert orc.planner_key_blocks(cfg, 0) == []
+
+
+def test_planner_order_contract():
+    T, d = 2, 4
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=1, head_dim=d, n_latents=81)
+    ro = orc.Rollout(cfg)
+    z = np.zeros((3 * T, 1, d))
+    with pytest.raises(orc.ContractError):
+        ro.plan_attend(1, z, z, z)                  # block 0 not published
+    ro.plan_attend(0, z, z, z)                      # denoising call: publishes nothing
+    with pytest.raises(orc.ContractError):
+        ro.plan_attend(1, z, z, z)
+    with pytest.raises(orc.ContractError):          # renderer chunk 0 needs anchors 0, 1
+        ro.render_attend(0, 0, z, z, z)
+    ro.plan_attend(0, z, z, z, publish=True)
+    with pytest.raises(orc.ContractError):
+        ro.plan_attend(0, z, z, z)                  # already published
+    ro.render_attend(0, 0, z, z, z)
+    with pytest.raises(orc.ContractError):
+        ro.plan_attend(3, z, z, z)                  # out of range (3 blocks)
+
+
+@pytest.mark.parametrize("target", ["oldest", "newest", "own"])
+def test_planner_each_source_reaches_the_output(target):
+    """A query pointed at one key of one source returns that key's value."""
+    T, d = 2, 64
+    eye = np.eye(d)
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=1, head_dim=d, n_latents=261)
+    ro = orc.Rollout(cfg)
+    b = 7                                           # reads blocks 1..6
+    for x in range(b):
+        K = np.zeros((3 * T, 1, d))
+        V = np.zeros((3 * T, 1, d))
+        for j, a in enumerate(range(3 * x, 3 * x + 3)):
+            K[j * T, 0] = eye[a]
+            V[j * T:(j + 1) * T] = 10.0 + a
+        ro.plan_attend(x, np.zeros((3 * T, 1, d)), K, V, publish=True, compute=False)
+    Kown = np.zeros((3 * T, 1, d))
+    Kown[0, 0] = eye[60]
+    Vown = np.full((3 * T, 1, d), 500.0)
+    key, val = {"oldest": (eye[3], 13.0), "newest": (eye[20], 30.0), "own": (eye[60], 500.0)}[target]
+    Q = np.zeros((3 * T, 1, d))
+    Q[:, 0] = 400.0 * key                           # score 50 against 0 for every other key
+    O, _ = ro.plan_attend(b, Q, Kown, Vown)
+    np.testing.assert_allclose(O[:, 0, :], val, atol=1e-9)
+    # block 0's anchors (0..2) are outside the window of block 7
+    Q[:, 0] = 400.0 * eye[1]
+    O, _ = ro.plan_attend(b, Q, Kown, Vown)
+    assert np.all(np.abs(O[:, 0, :] - 1.0 * 11.0) > 1.0)
