@@ -12,7 +12,8 @@
 
 namespace ff {
 
-constexpr int kMaxSeg = 12;        // <= 3 anchors + 8 history chunks + own chunk
+constexpr int kMaxSeg = 24;        // renderer: <= 3 anchors + 8 history chunks + own chunk;
+                                   // planner: one per anchor latent (<= W_ctx)
 constexpr int kMaxPairs = 8;       // renderer calls fused into one launch
 constexpr int kMaxHistory = 8;
 constexpr int kBlockM = 256;       // query rows per attention work item (8 waves x 32)
@@ -58,6 +59,8 @@ struct AttnLaunch {
   float scale;                     // 1/sqrt(d)
   int64_t slot_floats;             // floats per partial slot: O [BM][d], m [BM], l [BM]
 };
+// Passed by value as the kernel argument block, which is limited to 4 KB.
+static_assert(sizeof(AttnLaunch) <= 4096, "attention launch arguments exceed the kernel argument limit");
 
 // Layout copies between token-major rows and bank blocks.  A job moves `nseg`
 // consecutive sources of L tokens each: token-major rows [nseg*L][nh][d] on

@@ -18,7 +18,7 @@ using namespace ff;
 struct ff_ctx {
   ff_shape shape;
   int S = 0, H = 0;
-  int n_anchor = 0, n_chunk = 0;
+  int n_anchor = 0, n_chunk = 0, n_block = 0;   // anchors, renderer chunks, planner blocks
   int64_t T = 0, Lq = 0;          // tokens per latent, tokens per chunk
   int64_t esz = 2;
   uint8_t* ws = nullptr;
@@ -53,8 +53,14 @@ bool shape_ok(const ff_shape* s, int S, int H) {
   if (s->dtype != FF_BF16 && s->dtype != FF_F32) return false;
   if (s->gamma_rule != FF_GAMMA_BRACKET && s->gamma_rule != FF_GAMMA_CENTER_LR) return false;
   if (S < 1 || S > 64 || H < 1 || H > kMaxHistory) return false;
-  // query rows per chunk times heads must index in 32 bits
-  const int64_t lq = int64_t(s->chunk_latents) * s->tokens_per_latent;
+  if (s->planner_latents < 1 || s->planner_history < 0 || s->planner_history > 1024) return false;
+  // A planner call reads one source per anchor latent, at most W_ctx of them
+  // (and never more than its window holds).
+  const int64_t plan_src = std::min<int64_t>(int64_t(s->planner_history) * s->planner_latents + s->planner_latents,
+                                             std::max<int64_t>(s->w_ctx, s->planner_latents));
+  if (plan_src > kMaxSeg) return false;
+  // query rows per call times heads must index in 32 bits
+  const int64_t lq = int64_t(std::max(s->chunk_latents, s->planner_latents)) * s->tokens_per_latent;
   if (lq * s->n_heads * s->head_dim > (int64_t(1) << 31) - 1) return false;
   return true;
 }
@@ -101,6 +107,15 @@ int gamma_of(const ff_ctx* c, int i, int* ids) {
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool lse_ok(const float* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+uint8_t* anchor_ptr(const ff_ctx* c, int a) { return c->ws + c->anchor_off + size_t(a) * c->anchor_block; }
+
+// Anchors of planner block b: [b*B_P, b*B_P + n).
+int block_anchors(const ff_ctx* c, int b, int* first) {
+  const int bp = c->shape.planner_latents;
+  *first = b * bp;
+  return std::min(bp, c->n_anchor - b * bp);
+}
+
 uint8_t* slot_ptr(const ff_ctx* c, int stage, int chunk) {
   const int s = chunk % (c->H + 1);
   return c->ws + c->slot_off + (size_t(stage) * size_t(c->H + 1) + size_t(s)) * c->slot_block;
@@ -116,6 +131,41 @@ ff_status check_call(const ff_ctx* c, int i, int k) {
   for (int j = 0; j < n; ++j)
     if (!c->anchor_present[ids[j]]) return FF_E_ANCHOR_MISSING;
   return FF_OK;
+}
+
+// Order contract of planner block b (no side effects): every earlier block
+// published, the block itself not.
+ff_status check_plan(const ff_ctx* c, int b) {
+  if (b < 0 || b >= c->n_block) return FF_E_RANGE;
+  int first = 0;
+  const int n = block_anchors(c, b, &first);
+  for (int a = 0; a < first; ++a)
+    if (!c->anchor_present[a]) return FF_E_ORDER;
+  for (int a = first; a < first + n; ++a)
+    if (c->anchor_present[a]) return FF_E_ANCHOR_EXISTS;
+  return FF_OK;
+}
+
+// Key sources of planner block b: the anchors of the previous min(b, H_P)
+// blocks (oldest first, oldest blocks dropped while over W_ctx), then one
+// FF_SRC_OWN entry per anchor of the block.
+void plan_planner(const ff_ctx* c, int b, ff_key_sources* p) {
+  std::memset(p, 0, sizeof(*p));
+  const int bp = c->shape.planner_latents;
+  int first = 0;
+  const int n_own = block_anchors(c, b, &first);
+  int h_first = std::max(0, b - c->shape.planner_history);
+  while (h_first < b && bp * (b - h_first) + n_own > c->shape.w_ctx) ++h_first;
+  int n = 0;
+  for (int a = h_first * bp; a < b * bp; ++a) {
+    p->kind[n] = FF_SRC_ANCHOR; p->id[n] = a; p->n_tokens[n] = int32_t(c->T); ++n;
+  }
+  for (int a = first; a < first + n_own; ++a) {
+    p->kind[n] = FF_SRC_OWN; p->id[n] = a; p->n_tokens[n] = int32_t(c->T); ++n;
+  }
+  p->n_sources = n;
+  p->key_latents = n;
+  p->key_tokens = int32_t(int64_t(n) * c->T);
 }
 
 // Key sources of (i, k): Gamma(i) anchors ascending, then B_k^(i) oldest
@@ -142,13 +192,14 @@ void plan_of(const ff_ctx* c, int i, int k, ff_key_sources* p) {
   p->key_tokens = int32_t(tot);
 }
 
+// Device addresses of a call's sources.  k < 0 marks a planner call, whose
+// own latents are staged in their anchor-bank entries.
 void seg_table_of(const ff_ctx* c, int k, const ff_key_sources& p, SegTable* t) {
   std::memset(t, 0, sizeof(*t));
   int32_t tiles = 0;
   for (int j = 0; j < p.n_sources; ++j) {
-    const uint8_t* base = p.kind[j] == FF_SRC_ANCHOR
-                              ? c->ws + c->anchor_off + size_t(p.id[j]) * c->anchor_block
-                              : slot_ptr(c, k, p.id[j]);
+    const bool in_anchor_bank = p.kind[j] == FF_SRC_ANCHOR || (k < 0 && p.kind[j] == FF_SRC_OWN);
+    const uint8_t* base = in_anchor_bank ? anchor_ptr(c, p.id[j]) : slot_ptr(c, k, p.id[j]);
     t->base[j] = base;
     t->n[j] = p.n_tokens[j];
     t->tile_start[j] = tiles;
@@ -162,14 +213,14 @@ void seg_table_of(const ff_ctx* c, int k, const ff_key_sources& p, SegTable* t) 
 // units of each call are spread evenly over one persistent workgroup per CU.
 // The partition of a call depends only on that call, so it gives the same bits
 // alone or inside a grouped launch.
-void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_sources* plans,
+void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_sources* plans, int64_t lq,
                     const void* const* Q, void* const* O, float* const* lse, AttnLaunch* a) {
   std::memset(a, 0, sizeof(*a));
   a->n_pairs = n_pairs;
   a->nh = c->shape.n_heads;
   a->d = c->shape.head_dim;
-  a->lq = int32_t(c->Lq);
-  a->n_qtiles = int32_t((c->Lq + kBlockM - 1) / kBlockM);
+  a->lq = int32_t(lq);
+  a->n_qtiles = int32_t((lq + kBlockM - 1) / kBlockM);
   a->n_wg = kCUs;
   a->dtype = c->shape.dtype;
   a->scale = float(1.0 / std::sqrt(double(c->shape.head_dim)));
@@ -228,6 +279,7 @@ ff_status ff_stage_bank_create(const ff_shape* shape, int n_stages, int history,
   c->H = history;
   c->n_anchor = L.n_anchor;
   c->n_chunk = L.n_chunk;
+  c->n_block = (L.n_anchor + shape->planner_latents - 1) / shape->planner_latents;
   c->T = shape->tokens_per_latent;
   c->Lq = int64_t(shape->tokens_per_latent) * shape->chunk_latents;
   c->esz = elem_size(shape->dtype);
@@ -316,7 +368,7 @@ ff_status ff_render_attend_grouped(ff_ctx* c, int n_pairs, const int* chunks, co
 
   // 2) Segmented attention over anchors + history + own (now in the bank).
   AttnLaunch al;
-  fill_attention(c, n_pairs, stages, plans, Q, O, lse, &al);
+  fill_attention(c, n_pairs, stages, plans, c->Lq, Q, O, lse, &al);
   if (dev_launch_attention(al, stream, prof) != 0) return FF_E_HIP;
 
   for (int p = 0; p < n_pairs; ++p) {
@@ -334,6 +386,55 @@ ff_status ff_render_attend(ff_ctx* c, int chunk, int stage, const void* Q, const
   void* o[1] = {O};
   float* l[1] = {lse};
   return ff_render_attend_grouped(c, 1, &chunk, &stage, q, k, v, o, l, stream);
+}
+
+ff_status ff_plan_attend(ff_ctx* c, int block, const void* Q, const void* K, const void* V, void* O, float* lse,
+                         int publish, void* stream) {
+  if (!c || !aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !lse_ok(lse)) return FF_E_INVAL;
+  const ff_status st = check_plan(c, block);
+  if (st != FF_OK) return st;
+  ff_key_sources plan;
+  plan_planner(c, block, &plan);
+  int first = 0;
+  const int n_own = block_anchors(c, block, &first);
+
+  // 1) Stage the block's in-flight K/V in its anchor-bank entries.
+  CopyLaunch cl;
+  std::memset(&cl, 0, sizeof(cl));
+  cl.n_jobs = 1;
+  cl.max_nseg = n_own;
+  cl.L = int32_t(c->T);
+  cl.nh = c->shape.n_heads;
+  cl.d = c->shape.head_dim;
+  cl.dtype = c->shape.dtype;
+  cl.block_stride = int64_t(c->anchor_block);
+  cl.job[0].rows_k = K;
+  cl.job[0].rows_v = V;
+  cl.job[0].block = anchor_ptr(c, first);
+  cl.job[0].nseg = n_own;
+  Profiler* prof = c->profiling ? c->prof : nullptr;
+  if (dev_launch_publish(cl, stream, prof, true) != 0) return FF_E_HIP;
+
+  // 2) Segmented attention over the earlier blocks' anchors and its own.
+  AttnLaunch al;
+  const int stage = -1;
+  void* o[1] = {O};
+  const void* q[1] = {Q};
+  float* l[1] = {lse};
+  fill_attention(c, 1, &stage, &plan, int64_t(n_own) * c->T, q, o, l, &al);
+  if (dev_launch_attention(al, stream, prof) != 0) return FF_E_HIP;
+
+  if (publish)
+    for (int a = first; a < first + n_own; ++a) c->anchor_present[a] = 1;
+  return FF_OK;
+}
+
+ff_status ff_plan_key_plan(const ff_ctx* c, int block, ff_key_sources* out) {
+  if (!c || !out) return FF_E_INVAL;
+  const ff_status st = check_plan(c, block);
+  if (st != FF_OK) return st;
+  plan_planner(c, block, out);
+  return FF_OK;
 }
 
 ff_status ff_bank_tail(const ff_ctx* c, int stage, int* n_out, int* chunk_ids, void* K_out, void* V_out,

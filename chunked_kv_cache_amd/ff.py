@@ -21,13 +21,13 @@ FF_E_RANGE, FF_E_NOSPACE, FF_E_HIP, FF_E_STATE = -5, -6, -7, -8
 FF_BF16, FF_F32 = 0, 1
 FF_GAMMA_BRACKET, FF_GAMMA_CENTER_LR = 0, 1
 FF_SRC_ANCHOR, FF_SRC_HISTORY, FF_SRC_OWN = 0, 1, 2
-FF_MAX_SOURCES = 16
+FF_MAX_SOURCES = 32
 
 
 class ff_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_heads", "head_dim", "tokens_per_latent", "chunk_latents", "anchor_stride",
-        "n_latents", "w_ctx", "dtype", "gamma_rule")]
+        "n_latents", "w_ctx", "dtype", "gamma_rule", "planner_latents", "planner_history")]
 
 
 class ff_key_sources(ctypes.Structure):
@@ -63,6 +63,8 @@ _SIGS = {
     "ff_render_attend_grouped": (_I, [_VP, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), _VP]),
+    "ff_plan_attend": (_I, [_VP, _I, _VP, _VP, _VP, _VP, _VP, _I, _VP]),
+    "ff_plan_key_plan": (_I, [_VP, _I, ctypes.POINTER(ff_key_sources)]),
     "ff_bank_tail": (_I, [_VP, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), _VP, _VP, _VP]),
     "ff_gamma": (_I, [_VP, _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
     "ff_key_plan": (_I, [_VP, _I, _I, ctypes.POINTER(ff_key_sources)]),
@@ -120,9 +122,10 @@ def _check(st: int, L) -> None:
 
 
 def make_shape(*, n_heads, head_dim, tokens_per_latent, chunk_latents=3, anchor_stride=10, n_latents=81,
-               w_ctx=21, dtype=FF_BF16, gamma_rule=FF_GAMMA_BRACKET) -> ff_shape:
+               w_ctx=21, dtype=FF_BF16, gamma_rule=FF_GAMMA_BRACKET, planner_latents=3,
+               planner_history=6) -> ff_shape:
     return ff_shape(n_heads, head_dim, tokens_per_latent, chunk_latents, anchor_stride, n_latents, w_ctx,
-                    dtype, gamma_rule)
+                    dtype, gamma_rule, planner_latents, planner_history)
 
 
 def ff_workspace_bytes(shape: ff_shape, n_stages: int, history: int, L=None) -> int:
@@ -162,6 +165,19 @@ def ff_render_attend_grouped(ctx, chunks: Sequence[int], stages: Sequence[int], 
     lse_arr = None if lse is None else arr(lse)
     _check(L.ff_render_attend_grouped(ctx, n, (_I * n)(*chunks), (_I * n)(*stages), arr(Q), arr(K), arr(V),
                                       arr(O), lse_arr, _stream(stream, Q[0])), L)
+
+
+def ff_plan_attend(ctx, block, Q, K, V, O, lse=None, publish=False, stream=None, L=None) -> None:
+    L = L or lib()
+    _check(L.ff_plan_attend(ctx, block, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse), 1 if publish else 0,
+                            _stream(stream, Q)), L)
+
+
+def ff_plan_key_plan(ctx, block, L=None) -> ff_key_sources:
+    L = L or lib()
+    out = ff_key_sources()
+    _check(L.ff_plan_key_plan(ctx, block, ctypes.byref(out)), L)
+    return out
 
 
 def ff_bank_tail(ctx, stage, K_out=None, V_out=None, stream=None, L=None, history_max=8):

@@ -44,8 +44,9 @@ extern "C" {
 typedef enum {
   FF_OK = 0,
   FF_E_INVAL = -1,           /* null / misaligned pointer, unsupported shape   */
-  FF_E_ORDER = -2,           /* (i,k) is not the next call of stage k, or      */
-                             /* chunk i has not run stage k-1 yet              */
+  FF_E_ORDER = -2,           /* (i,k) is not the next call of stage k, chunk i */
+                             /* has not run stage k-1 yet, or an earlier      */
+                             /* planner block is unpublished                  */
   FF_E_ANCHOR_MISSING = -3,  /* an anchor of Gamma(i) is not published         */
   FF_E_ANCHOR_EXISTS = -4,   /* anchor already published (append-only bank)    */
   FF_E_RANGE = -5,           /* chunk, stage or anchor id out of range         */
@@ -66,8 +67,9 @@ typedef enum { FF_BF16 = 0, FF_F32 = 1 } ff_dtype;
  *                      the next one (always 2 inside the clip).               */
 typedef enum { FF_GAMMA_BRACKET = 0, FF_GAMMA_CENTER_LR = 1 } ff_gamma_rule;
 
-/* Static shape of one attention layer of the renderer.  [S] "how it differs":
- * B_R = 3 latents per chunk, Delta = 10, W_ctx = 21; 81 latents per clip.    */
+/* Static shape of one attention layer.  [S] "how it differs": B_R = 3
+ * latents per chunk, B_P = 3 anchors per planner block, Delta = 10,
+ * W_ctx = 21, H_P = 6; 81 latents per clip.                                 */
 typedef struct {
   int32_t n_heads;            /* >= 1                                         */
   int32_t head_dim;           /* 64 or 128                                    */
@@ -79,13 +81,16 @@ typedef struct {
                               /* dropped first beyond it)                     */
   int32_t dtype;              /* ff_dtype                                     */
   int32_t gamma_rule;         /* ff_gamma_rule                                */
+  int32_t planner_latents;    /* B_P: anchors per planner block, >= 1         */
+  int32_t planner_history;    /* H_P: earlier planner blocks a planner block  */
+                              /* attends, >= 0 ([S] "how it differs": 6)      */
 } ff_shape;
 
 typedef struct ff_ctx ff_ctx;                    /* opaque host-side state    */
 
 /* Key sources of one call, in the order attention sees them. */
 enum { FF_SRC_ANCHOR = 0, FF_SRC_HISTORY = 1, FF_SRC_OWN = 2 };
-#define FF_MAX_SOURCES 16
+#define FF_MAX_SOURCES 32
 typedef struct {
   int32_t n_sources;
   int32_t kind[FF_MAX_SOURCES];      /* FF_SRC_*                              */
@@ -183,6 +188,30 @@ ff_status ff_stage_next(const ff_ctx* ctx, int stage, int* next_chunk);
  * FF_E_STATE.  Host metadata only; enqueues nothing.  Not in the pages.       */
 ff_status ff_stage_bank_rewind(ff_ctx* ctx, int stage);
 
+/* ff_plan_attend -- one planner-role attention call of planner block `block`
+ * (anchors block*B_P .. block*B_P + n_b - 1, n_b = B_P except a shorter last
+ * block).  [S] "how it differs": anchors are generated B_P at a time and one
+ * cache-extraction forward per completed block publishes the block's clean
+ * anchor KV; [S] training paragraph: a planner block attends causally to the
+ * clean KV of earlier blocks.  Reading taken (not printed on the pages): the
+ * block attends the published anchors of the previous min(block, H_P) blocks
+ * (oldest first; oldest blocks dropped while the key latents exceed W_ctx)
+ * plus its own in-flight K/V, no mask.
+ * Q, K, V, O: [n_b*T][n_heads][head_dim]; lse as for ff_render_attend.
+ * The block's K/V are staged in its own anchor-bank entries; with publish != 0
+ * the call is the cache-extraction forward and those anchors become published
+ * (usable by renderer calls), else they stay unpublished and the next call
+ * of the block overwrites them.  Order contract: every earlier block
+ * published (else FF_E_ORDER) and the block itself not (FF_E_ANCHOR_EXISTS).
+ * ff_anchor_bank_publish remains the way to publish anchors computed
+ * elsewhere.                                                                  */
+ff_status ff_plan_attend(ff_ctx* ctx, int block, const void* Q, const void* K, const void* V,
+                         void* O, float* lse, int publish, void* stream);
+/* ff_plan_key_plan -- the key sources ff_plan_attend(block) would read in the
+ * current state: FF_SRC_ANCHOR entries for earlier blocks' anchors, then one
+ * FF_SRC_OWN entry per anchor of the block (id = anchor id).  Host only;
+ * validates the order contract exactly like ff_plan_attend.                   */
+ff_status ff_plan_key_plan(const ff_ctx* ctx, int block, ff_key_sources* out);
 /* Per-kernel device timing: while enabled, each launch is bracketed by HIP
  * events on its stream; ff_profile_read synchronises those events and returns
  * the accumulated totals since enabling (enable also resets them).            */

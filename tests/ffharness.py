@@ -53,17 +53,19 @@ class Case:
     rule: str = orc.GAMMA_BRACKET
     seed: int = 0
     q_scale: float = 1.0
+    h_p: int = 6
 
     @property
     def cfg(self) -> orc.FFConfig:
         return orc.FFConfig(tokens_per_latent=self.T, n_heads=self.nh, head_dim=self.d, n_latents=self.n_latents,
-                            n_stages=self.S, history=self.H, w_ctx=self.w_ctx, gamma_rule=self.rule)
+                            n_stages=self.S, history=self.H, w_ctx=self.w_ctx, gamma_rule=self.rule,
+                            planner_history=self.h_p)
 
     def shape(self) -> ff.ff_shape:
         return ff.make_shape(n_heads=self.nh, head_dim=self.d, tokens_per_latent=self.T, n_latents=self.n_latents,
                              w_ctx=self.w_ctx, dtype=ff.FF_BF16 if self.dtype == "bf16" else ff.FF_F32,
                              gamma_rule=ff.FF_GAMMA_BRACKET if self.rule == orc.GAMMA_BRACKET
-                             else ff.FF_GAMMA_CENTER_LR)
+                             else ff.FF_GAMMA_CENTER_LR, planner_history=self.h_p)
 
 
 @dataclass
@@ -167,6 +169,43 @@ class Pair:
             if check_bank:
                 self.check_bank(k)
         return results
+
+    def plan_step(self, b: int, step: int, publish: bool, rows: Optional[np.ndarray] = None,
+                  control: bool = False):
+        """One planner call of block b at denoising step `step` on the GPU, then the oracle."""
+        import torch
+        c = self.case
+        blk = orc.planner_blocks(self.cfg)[b]
+        n = len(blk) * c.T
+        host = syn.planner_qkv(T=c.T, n_heads=c.nh, head_dim=c.d, block=b, step=step, n_latents=len(blk),
+                               seed=c.seed, dtype=c.dtype, q_scale=c.q_scale)
+        dq, dk, dv = (to_device(x, c.dtype) for x in host)
+        tdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        out = torch.full_like(dq, float("nan"), dtype=tdt)
+        lse = torch.full((c.nh, n), float("nan"), dtype=torch.float32, device="cuda")
+        ff.ff_plan_attend(self.ctx, b, dq, dk, dv, out, lse, publish=publish)
+        torch.cuda.synchronize()
+        q64, k64, v64 = (syn.as_f64(x, c.dtype) for x in host)
+        srcs = self.ro.plan_key_sources(b)
+        vkeys = max([self.vmax[("anchor", a)] for kind, a in srcs if kind == "anchor"] +
+                    [float(np.abs(v64).max())])
+        ctrl = None
+        if control:
+            qc = q64 if rows is None else q64[rows]
+            ctrl, _ = orc.attention(qc, k64, v64, self.cfg.scale)        # own latents only
+        O_ref, L_ref = self.ro.plan_attend(b, q64, k64, v64, publish=publish, rows=rows)
+        O = from_device_f64(out)
+        L = lse.cpu().numpy().astype(np.float64)
+        if rows is not None:
+            O, L = O[rows], L[:, rows]
+        tol = TOL[c.dtype]
+        if c.dtype == "bf16":
+            tol = max(tol, bf16_rounding_bound(O_ref, vkeys))
+        self._compare(O, L, O_ref, L_ref, ctrl, tol)
+        if publish:
+            for j, a in enumerate(blk):
+                self.vmax[("anchor", a)] = float(np.abs(v64[j * c.T:(j + 1) * c.T]).max())
+        return O, O_ref
 
     def _control(self, i, k, host, rows):
         """Negative control: the oracle with the anchor sources dropped."""

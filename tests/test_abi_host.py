@@ -79,7 +79,8 @@ class HostCtx:
         self.shape = ff.make_shape(n_heads=cfg.n_heads, head_dim=cfg.head_dim,
                                    tokens_per_latent=cfg.tokens_per_latent, chunk_latents=cfg.chunk_latents,
                                    anchor_stride=cfg.anchor_stride, n_latents=cfg.n_latents,
-                                   w_ctx=cfg.w_ctx if w_ctx is None else w_ctx, dtype=dtype, gamma_rule=rule)
+                                   w_ctx=cfg.w_ctx if w_ctx is None else w_ctx, dtype=dtype, gamma_rule=rule,
+                                   planner_latents=cfg.planner_block, planner_history=cfg.planner_history)
         self.need = ff.ff_workspace_bytes(self.shape, cfg.n_stages, cfg.history, L=self.L)
         self.raw, self.ws = _aligned_buffer(self.need)
         self.ctx = ff.ff_stage_bank_create(self.shape, cfg.n_stages, cfg.history, self.ws, self.need, L=self.L)
@@ -90,8 +91,8 @@ class HostCtx:
         return [x.value for x in c]
 
     def last_segments(self, p=0):
-        off = (ctypes.c_longlong * 16)()
-        n = (ctypes.c_int * 16)()
+        off = (ctypes.c_longlong * ff.FF_MAX_SOURCES)()
+        n = (ctypes.c_int * ff.FF_MAX_SOURCES)()
         lk, ns = ctypes.c_int(), ctypes.c_int()
         f = self.L.ffstub_last_segments
         f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -310,3 +311,86 @@ def test_history_and_workspace_limits():
     with pytest.raises(ff.FFError) as e:
         ff.ff_stage_bank_create(shape, 4, 5, 256 + 16, need, L=L)     # workspace not 256-aligned
     assert e.value.status == ff.FF_E_INVAL
+
+
+# --------------------------------------------------------------------------
+# Planner calls
+# --------------------------------------------------------------------------
+def _plan_sources(ks: "ff.ff_key_sources"):
+    kinds = {ff.FF_SRC_ANCHOR: "anchor", ff.FF_SRC_OWN: "own"}
+    return [(kinds[ks.kind[j]], ks.id[j]) for j in range(ks.n_sources)]
+
+
+@pytest.mark.parametrize("L,h_p,w_ctx", [(261, 6, 21), (261, 2, 21), (261, 6, 11), (81, 6, 21)])
+def test_planner_key_plan_and_launch_match_oracle(L, h_p, w_ctx):
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=64, n_latents=L, planner_history=h_p,
+                       w_ctx=w_ctx)
+    hc = HostCtx(cfg)
+    ro = orc.Rollout(cfg)
+    anchor_block, _, _ = _layout(cfg)
+    T = cfg.tokens_per_latent
+    z = np.zeros((3 * T, 2, 64))
+    try:
+        for b, blk in enumerate(orc.planner_blocks(cfg)):
+            for publish in (False, True):
+                want = ro.plan_key_sources(b)
+                ks = ff.ff_plan_key_plan(hc.ctx, b, L=hc.L)
+                assert _plan_sources(ks) == want
+                assert ks.key_tokens == T * len(want) and ks.key_latents == len(want)
+                before = hc.counts()
+                ff.ff_plan_attend(hc.ctx, b, FAKE, FAKE, FAKE, FAKE, None, publish=publish, L=hc.L)
+                after = hc.counts()
+                assert [a - c for a, c in zip(after, before)] == [1, 0, 1, 0]   # attention + anchor-bank copy
+                off, n, lk, ntiles = hc.last_segments()
+                assert off == [a * anchor_block for _, a in want]
+                assert n == [T] * len(want) and lk == T * len(want)
+                assert ntiles == len(want) * ((T + 63) // 64)
+                assert hc.last_copy_block(0) == blk[0] * anchor_block
+                ro.plan_attend(b, z[:len(blk) * T], z[:len(blk) * T], z[:len(blk) * T], publish=publish,
+                               compute=False)
+    finally:
+        hc.close()
+
+
+def test_planner_order_contract_and_atomicity():
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=64, n_latents=81)
+    hc = HostCtx(cfg)
+    try:
+        def status(fn):
+            try:
+                fn()
+                return ff.FF_OK
+            except ff.FFError as e:
+                return e.status
+        plan = lambda b, pub=False: status(lambda: ff.ff_plan_attend(hc.ctx, b, FAKE, FAKE, FAKE, FAKE, None,
+                                                                      publish=pub, L=hc.L))
+        before = hc.counts()
+        assert plan(1) == ff.FF_E_ORDER
+        assert plan(3) == ff.FF_E_RANGE and plan(-1) == ff.FF_E_RANGE
+        assert status(lambda: ff.ff_plan_attend(hc.ctx, 0, FAKE + 8, FAKE, FAKE, FAKE, L=hc.L)) == ff.FF_E_INVAL
+        assert hc.counts() == before                                 # nothing launched
+        assert plan(0) == ff.FF_OK                                   # denoising call: publishes nothing
+        assert status(lambda: ff.ff_render_attend(hc.ctx, 0, 0, FAKE, FAKE, FAKE, FAKE, L=hc.L)) == \
+            ff.FF_E_ANCHOR_MISSING
+        assert plan(1) == ff.FF_E_ORDER
+        assert plan(0, True) == ff.FF_OK                             # cache-extraction call
+        assert plan(0) == ff.FF_E_ANCHOR_EXISTS
+        assert status(lambda: ff.ff_anchor_bank_publish(hc.ctx, 0, 3, FAKE, FAKE, L=hc.L)) == \
+            ff.FF_E_ANCHOR_EXISTS
+        assert status(lambda: ff.ff_render_attend(hc.ctx, 0, 0, FAKE, FAKE, FAKE, FAKE, L=hc.L)) == ff.FF_OK
+        # block 1 may also be published by the plain anchor publish after its denoising calls
+        assert plan(1) == ff.FF_OK
+        ff.ff_anchor_bank_publish(hc.ctx, 3, 3, FAKE, FAKE, L=hc.L)
+        assert plan(1) == ff.FF_E_ANCHOR_EXISTS and plan(2) == ff.FF_OK
+    finally:
+        hc.close()
+
+
+def test_planner_shape_limits():
+    L = ff.load(ff.HOSTCHECK_PATH)
+    ok = ff.make_shape(n_heads=2, head_dim=64, tokens_per_latent=16)
+    assert ff.ff_workspace_bytes(ok, 4, 5, L=L) > 0
+    for kw in (dict(planner_latents=0), dict(planner_history=-1),
+               dict(planner_history=9, w_ctx=30)):                   # 30 planner sources > 24
+        bad = ff.make_shape(n_heads=2, head_dim=64, tokens_per_latent=16, **kw)
+        assert ff.ff_workspace_bytes(bad, 4, 5, L=L) == 0, kw

@@ -119,6 +119,62 @@ def test_minimum_tokens_and_single_history():
     assert st.calls == 54
 
 
+def _planner_rollout(case, steps=2, rows=None, render_diags=0, control=True):
+    """Every planner block in order: `steps` denoising calls, then the
+    cache-extraction call that publishes the block; then the first
+    `render_diags` anti-diagonals of the renderer on the anchors so published."""
+    pr = Pair(case)
+    try:
+        for b in range(len(orc.planner_blocks(case.cfg))):
+            for step in range(steps):
+                pr.plan_step(b, step, publish=False, rows=rows, control=control and b > 0 and step == 0)
+            pr.plan_step(b, steps, publish=True, rows=rows)
+        for diag in orc.schedule(case.cfg)[:render_diags]:
+            pr.step(diag, grouped=True, rows=rows)
+        return pr.stats
+    finally:
+        pr.close()
+
+
+def test_planner_rollout_tiny_fp32():
+    """fp32, 2 heads, d=64, T=16, 261 latents: 9 planner blocks x (2 denoising
+    calls + the cache-extraction call), then 12 renderer diagonals on them."""
+    st = _planner_rollout(Case(T=16, nh=2, d=64, dtype="f32", n_latents=261, S=2), render_diags=12)
+    assert st.calls == 27 + 23
+    print(f"planner fp32: max|dO|={st.max_abs:.2e} relF={st.max_rel_fro:.2e} lse={st.max_lse:.2e}")
+
+
+@pytest.mark.parametrize("h_p", [6, 2])
+def test_planner_rollout_bf16_multi_tile(h_p):
+    """bf16, T=120 (360 queries: 2 query tiles, ragged), 261 latents: block 8
+    reads min(8, H_P) earlier blocks (up to 18 anchors + 3 own = 6720 keys,
+    each anchor a ragged 64-key source)."""
+    st = _planner_rollout(Case(T=120, nh=2, d=128, n_latents=261, S=2, h_p=h_p), render_diags=4)
+    assert st.calls == 27 + 7
+    print(f"planner bf16 H_P={h_p}: max|dO|={st.max_abs:.2e} relF={st.max_rel_fro:.2e} "
+          f"control>={st.min_control_ratio:.1f}x")
+
+
+def test_planner_480p_block_sampled_rows():
+    """480p shape, 261 latents: blocks 0..8 published through their
+    cache-extraction calls; block 8's denoising call reads 6 earlier blocks
+    (21 key latents, 4680 queries x 32760 keys), 32 sampled rows per call."""
+    import sys
+    case = Case(T=1560, nh=12, d=128, n_latents=261, S=1)
+    rows = np.sort(np.random.default_rng(3).choice(3 * 1560, size=32, replace=False))
+    pr = Pair(case)
+    try:
+        for b in range(9):
+            if b == 8:
+                pr.plan_step(b, 0, publish=False, rows=rows, control=True)
+            pr.plan_step(b, 1, publish=True, rows=rows)
+            print(f"  planner block {b} ok", flush=True, file=sys.stderr)
+        print(f"planner 480p: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
+              f"control>={pr.stats.min_control_ratio:.1f}x")
+    finally:
+        pr.close()
+
+
 def test_480p_steps_sampled_rows():
     """480p shape (T=1560, 12 heads, d=128) at stage 0, chunks 0..13: chunk 5 is the
     first 20-latent step (31200 keys), chunk 13 the 21-latent one (32760 keys, three
