@@ -10,6 +10,11 @@ S = 4 stage banks (4 distinct key sets, 0.77 GB, more than the 256 MB
 last-level cache); before each round the four banks are rewound by one chunk
 (ff_stage_bank_rewind) so the same steady-state call repeats.
 
+`--workload plan480` measures the planner role instead: one step is one
+denoising ff_plan_attend call of planner block 8 of a 261-latent clip
+(staging of its K/V + attention over 6 earlier blocks' anchors and its own
+3 latents: 4680 queries x 32760 keys).
+
 Prints one JSON line.  `value` = attention TFLOP/s of the whole step
 (algorithmic 4*Lq*Lk*d*nh FLOPs / wall time per step).  `roofline` = the
 attention kernel alone, from HIP events on the launch stream.  `cpu_baseline`
@@ -37,6 +42,9 @@ WORKLOADS = {
                                          "32760 keys (3 anchors + 5 history + own), 12 heads x 128"),
     "step720": (3600, 40, 5, 81, 1, "720p renderer step: chunk 5, 10800 queries x 72000 keys "
                                     "(2 anchors + 5 history + own), 40 heads x 128"),
+    # planner role: block 8 of a 261-latent clip (27 anchors, 9 blocks of 3)
+    "plan480": (1560, 12, 8, 261, 1, "480p planner block step: block 8 of 261 latents, 4680 queries x 32760 "
+                                     "keys (18 anchors of 6 earlier blocks + own 3 latents), 12 heads x 128"),
 }
 
 
@@ -86,6 +94,8 @@ def main():
     import synthetic as syn
     from chunked_kv_cache_amd import ff
 
+    if args.workload.startswith("plan"):
+        return run_planner(args)
     T, nh, chunk, n_latents, S, desc = WORKLOADS[args.workload]
     d, H = 128, 5
     torch.cuda.set_device(0)
@@ -218,6 +228,123 @@ def main():
     banks.close()
 
 
+def run_planner(args):
+    """Planner-role workload: one step = one denoising ff_plan_attend call of a
+    planner block (staging of its K/V in the anchor bank + segmented attention
+    over the earlier blocks' anchors and its own latents).  The anchors of the
+    earlier blocks are published once; the repeated call changes no state, as
+    the denoising steps of one block do."""
+    import numpy as np
+    import torch
+
+    import synthetic as syn
+    from chunked_kv_cache_amd import ff
+
+    T, nh, block, n_latents, _, desc = WORKLOADS[args.workload]
+    d = 128
+    torch.cuda.set_device(0)
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16).cuda()
+    shape = ff.make_shape(n_heads=nh, head_dim=d, tokens_per_latent=T, n_latents=n_latents)
+    banks = ff.StageBanks(shape, 1, 5)
+    ctx = banks.ctx
+    t0 = time.time()
+    for a0 in range(0, 3 * block, 3):
+        blk = [a0, a0 + 1, a0 + 2]
+        K, V = syn.anchor_kv(T=T, n_heads=nh, head_dim=d, anchors=blk)
+        ff.ff_anchor_bank_publish(ctx, a0, 3, dev(K), dev(V))
+    host = syn.planner_qkv(T=T, n_heads=nh, head_dim=d, block=block, step=0, n_latents=3)
+    qd, kd, vd = (dev(x) for x in host)
+    Lq = 3 * T
+    out = torch.empty((Lq, nh, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((nh, Lq), dtype=torch.float32, device="cuda")
+    plan = ff.ff_plan_key_plan(ctx, block)
+    Lk = plan.key_tokens
+    flops = 4.0 * Lq * Lk * d * nh
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s")
+    for _ in range(args.warmup):
+        ff.ff_plan_attend(ctx, block, qd, kd, vd, out, lse, stream=stream)
+    torch.cuda.synchronize()
+    ff.ff_profile_enable(ctx, True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        ff.ff_plan_attend(ctx, block, qd, kd, vd, out, lse, stream=stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    prof = ff.ff_profile_read(ctx)
+    ff.ff_profile_enable(ctx, False)
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = flops * args.steps / wall / 1e12
+    attn_ms = prof["attn_ms"] / max(prof["attn_launches"], 1)
+    stage_us = 1e3 * prof["anchor_ms"] / max(prof["anchor_launches"], 1)
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+    log(f"attention kernel {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s), staging {stage_us:.1f} us, "
+        f"step {ms_per_step:.3f} ms")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_planner(host, block, T, nh, d, args.cpu_heads, n_latents)
+    res = {
+        "metric": "planner block-attention TFLOP/s (% bf16 MFMA peak)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V and anchors, 480p planner shapes)",
+        "config": {"workload": desc, "queries": Lq, "keys": Lk, "heads": nh, "head_dim": d,
+                   "tokens_per_latent": T, "block": block, "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "attention_kernel_ms": round(attn_ms, 4),
+        "staging_kernel_us": round(stage_us, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    banks.close()
+
+
+def cpu_baseline_planner(host_qkv, block, T, nh, d, n_heads_sample, n_latents):
+    """The float64 oracle's planner call for the same block on the first
+    `n_heads_sample` heads (key-source gather + attention)."""
+    import oracle as orc
+    import synthetic as syn
+    threads = _threads()
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=n_heads_sample, head_dim=d, n_latents=n_latents, n_stages=1)
+    ro = orc.Rollout(cfg)
+    hs = slice(0, n_heads_sample)
+    f64 = lambda x: syn.as_f64(x, "bf16")[:, hs]
+    for a in range(3 * block):
+        K, V = syn.anchor_kv(T=T, n_heads=nh, head_dim=d, anchors=[a])
+        ro.anchors[a] = (f64(K), f64(V))
+    q, kk, vv = (f64(x) for x in host_qkv)
+    n_keys = T * len(ro.plan_key_sources(block))
+    t0 = time.perf_counter()
+    ro.plan_attend(block, q, kk, vv)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * q.shape[0] * n_keys * d * n_heads_sample
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle planner call for block {block} ({n_keys} keys), {n_heads_sample} of "
+                      f"{nh} heads: {flops / 1e9:.0f} GFLOP in {dt:.1f} s"}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
+                   default=len(os.sched_getaffinity(0)))
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(ctx, host_qkv, chunk, T, nh, d, n_heads_sample, n_latents):
     """The float64 oracle on a bounded sample of the same workload: its whole
     renderer call (order checks, gather of the key sources, attention, Tail_H
@@ -226,12 +353,7 @@ def cpu_baseline(ctx, host_qkv, chunk, T, nh, d, n_heads_sample, n_latents):
     import numpy as np
     import oracle as orc
     import synthetic as syn
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"),
-                      default=len(os.sched_getaffinity(0)))
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+    threads = _threads()
     cfg = orc.FFConfig(tokens_per_latent=T, n_heads=n_heads_sample, head_dim=d, n_latents=n_latents, n_stages=1)
     ro = orc.Rollout(cfg)
     hs = slice(0, n_heads_sample)
