@@ -184,13 +184,7 @@ def main():
         f"publish {pub_ms * 1e3:.1f} us ({pub_gbps:.0f} GB/s), step {ms_per_step:.3f} ms")
 
     if args.calibration_copy:
-        n = 64 << 20                                   # 64 Mi floats = 256 MiB each way
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.add(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log("calibration copy: 3 x (256 MiB read + 256 MiB write), kernel vectorized_elementwise add")
+        calibration_copy()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -226,6 +220,19 @@ def main():
     }
     print(json.dumps(out), flush=True)
     banks.close()
+
+
+def calibration_copy():
+    """A plain device copy of known size after the timed region: its rocprofv3
+    FETCH_SIZE / WRITE_SIZE scale those counters to bytes."""
+    import torch
+    n = 64 << 20                                   # 64 Mi floats = 256 MiB each way
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log("calibration copy: 3 x (256 MiB read + 256 MiB write), kernel vectorized_elementwise add")
 
 
 def run_planner(args):
@@ -282,6 +289,8 @@ def run_planner(args):
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     log(f"attention kernel {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s), staging {stage_us:.1f} us, "
         f"step {ms_per_step:.3f} ms")
+    if args.calibration_copy:
+        calibration_copy()
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_planner(host, block, T, nh, d, args.cpu_heads, n_latents)
