@@ -42,6 +42,15 @@ WORKLOADS = {
                                          "32760 keys (3 anchors + 5 history + own), 12 heads x 128"),
     "step720": (3600, 40, 5, 81, 1, "720p renderer step: chunk 5, 10800 queries x 72000 keys "
                                     "(2 anchors + 5 history + own), 40 heads x 128"),
+    "step480_warm": (1560, 12, 5, 81, 1, "480p renderer step, warm: chunk 5 repeated on one stage bank "
+                                         "(31200 keys, key set resident in the last-level cache)"),
+    # whole rollouts (T, nh, -, n_latents, S, description)
+    "rollout480": (1560, 12, 0, 81, 4, "480p 81-latent rollout: 9 anchors published, then 27 chunks x 4 stages "
+                                       "= 108 ff_render_attend calls in wavefront order, one call per launch"),
+    "rollout480_grouped": (1560, 12, 0, 81, 4, "480p 81-latent rollout as 30 grouped anti-diagonal launches "
+                                               "(108 calls)"),
+    "rollout65s": (1560, 12, 0, 261, 4, "480p 65 s rollout: 261 latents, 27 anchors, 87 chunks x 4 stages = "
+                                        "348 calls in 90 grouped anti-diagonal launches"),
     # planner role: block 8 of a 261-latent clip (27 anchors, 9 blocks of 3)
     "plan480": (1560, 12, 8, 261, 1, "480p planner block step: block 8 of 261 latents, 4680 queries x 32760 "
                                      "keys (18 anchors of 6 earlier blocks + own 3 latents), 12 heads x 128"),
@@ -96,6 +105,8 @@ def main():
 
     if args.workload.startswith("plan"):
         return run_planner(args)
+    if args.workload.startswith("rollout"):
+        return run_rollout(args)
     T, nh, chunk, n_latents, S, desc = WORKLOADS[args.workload]
     d, H = 128, 5
     torch.cuda.set_device(0)
@@ -233,6 +244,95 @@ def calibration_copy():
         torch.add(src, 1.0, out=dst)
     torch.cuda.synchronize()
     log("calibration copy: 3 x (256 MiB read + 256 MiB write), kernel vectorized_elementwise add")
+
+
+def run_rollout(args):
+    """Whole-rollout workloads: anchors published (untimed), then every
+    (chunk, stage) call of the wavefront schedule, timed end to end.  Inputs
+    come from a pool of 8 seeded N(0,1) bf16 Q/K/V sets drawn on the device
+    (values do not change the work; the pool keeps setup short)."""
+    import torch
+
+    import oracle as orc
+    from chunked_kv_cache_amd import ff
+
+    T, nh, _, n_latents, S, desc = WORKLOADS[args.workload]
+    d, H = 128, 5
+    grouped = args.workload != "rollout480"
+    torch.cuda.set_device(0)
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    Lq = 3 * T
+    randn = lambda n: torch.randn((n, nh, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    pool = [(randn(Lq), randn(Lq), randn(Lq)) for _ in range(8)]
+    shape = ff.make_shape(n_heads=nh, head_dim=d, tokens_per_latent=T, n_latents=n_latents)
+    banks = ff.StageBanks(shape, S, H)
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=nh, head_dim=d, n_latents=n_latents, n_stages=S)
+    sched = orc.schedule(cfg)
+    n_calls = sum(len(x) for x in sched)
+    outs = [torch.empty((Lq, nh, d), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+    blocks = orc.planner_blocks(cfg)
+    anchor_kv = [(randn(len(b) * T), randn(len(b) * T)) for b in blocks]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def rollout():
+        banks.close()
+        banks.ctx = ff.ff_stage_bank_create(shape, S, H, banks.workspace, banks.ws_bytes)
+        ctx = banks.ctx
+        for b, (K, V) in zip(blocks, anchor_kv):
+            ff.ff_anchor_bank_publish(ctx, b[0], len(b), K, V, stream=stream)
+        torch.cuda.synchronize()
+        flops = 0.0
+        j = 0
+        t0 = time.perf_counter()
+        for diag in sched:
+            plans = [ff.ff_key_plan(ctx, i, k) for i, k in diag]
+            flops += sum(4.0 * Lq * p.key_tokens * d * nh for p in plans)
+            sets = [pool[(j + n) % 8] for n in range(len(diag))]
+            j += len(diag)
+            if grouped:
+                ff.ff_render_attend_grouped(ctx, [i for i, _ in diag], [k for _, k in diag],
+                                            [x[0] for x in sets], [x[1] for x in sets], [x[2] for x in sets],
+                                            [outs[k] for _, k in diag], stream=stream)
+            else:
+                for (i, k), x in zip(diag, sets):
+                    ff.ff_render_attend(ctx, i, k, x[0], x[1], x[2], outs[k], stream=stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, flops
+
+    reps = max(1, min(args.steps, 5))
+    for _ in range(max(1, min(args.warmup, 2))):
+        rollout()
+    times = []
+    for _ in range(reps):
+        dt, flops = rollout()
+        times.append(dt)
+    dt = sorted(times)[len(times) // 2]
+    tflops = flops / dt / 1e12
+    log(f"rollout: {n_calls} calls in {len(sched)} diagonals, median {dt * 1e3:.1f} ms "
+        f"(min {min(times) * 1e3:.1f}), {flops / 1e12:.1f} TFLOP, {tflops:.1f} TFLOP/s, "
+        f"{n_calls / dt:.0f} chunk-steps/s")
+    res = {
+        "metric": "renderer rollout TFLOP/s (% bf16 MFMA peak) + chunk-steps/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": reps,
+        "warmup": max(1, min(args.warmup, 2)),
+        "ms_per_step": round(dt * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, a pool of 8 Q/K/V sets drawn on the device)",
+        "config": {"workload": desc, "calls": n_calls, "launches": len(sched) if grouped else n_calls,
+                   "heads": nh, "head_dim": d, "tokens_per_latent": T, "stage_banks": S, "history": H,
+                   "rollout_tflop": round(flops / 1e12, 2), "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "chunk_steps_per_s": round(n_calls / dt, 1),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    banks.close()
 
 
 def run_planner(args):
