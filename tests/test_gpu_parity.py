@@ -215,19 +215,20 @@ def test_480p_rollout_grouped_full_size():
 
 
 def test_720p_step_sampled_rows():
-    """720p / 14B shape (T=3600, 40 heads, d=128): chunks 0..5 at stage 0, chunk 5
-    is the 20-latent step (10800 queries x 72000 keys); 8 sampled query rows
-    per call against the oracle, banks exact."""
+    """720p / 14B shape (T=3600, 40 heads, d=128): chunks 0..13 at stage 0; chunk 5
+    is the 20-latent step (10800 queries x 72000 keys) and chunk 13 the
+    21-latent one (75600 keys, three anchors), the largest call of the
+    workloads; 8 sampled query rows per call against the oracle, banks exact."""
     import sys
     case = Case(T=3600, nh=40, d=128, S=1)
     rows = np.sort(np.random.default_rng(5).choice(3 * 3600, size=8, replace=False))
     pr = Pair(case, device_bank_check=True)
     try:
         pr.publish_anchors()
-        for i in range(6):
-            pr.step([(i, 0)], grouped=False, rows=rows, control=(i == 5))
+        for i in range(14):
+            pr.step([(i, 0)], grouped=False, rows=rows, control=i in (5, 13))
             print(f"  720p chunk {i} ok", flush=True, file=sys.stderr)
-        print(f"720p chunks 0..5: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
+        print(f"720p chunks 0..13: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
               f"control>={pr.stats.min_control_ratio:.1f}x")
     finally:
         pr.close()
