@@ -42,6 +42,8 @@ WORKLOADS = {
                                          "32760 keys (3 anchors + 5 history + own), 12 heads x 128"),
     "step720": (3600, 40, 5, 81, 1, "720p renderer step: chunk 5, 10800 queries x 72000 keys "
                                     "(2 anchors + 5 history + own), 40 heads x 128"),
+    "step720_21": (3600, 40, 13, 81, 1, "720p renderer step at the 21-latent cap: chunk 13, 10800 queries x "
+                                         "75600 keys (3 anchors + 5 history + own), 40 heads x 128"),
     "step480_warm": (1560, 12, 5, 81, 1, "480p renderer step, warm: chunk 5 repeated on one stage bank "
                                          "(31200 keys, key set resident in the last-level cache)"),
     # whole rollouts (T, nh, -, n_latents, S, description)
