@@ -4,3 +4,6 @@ from .flashforward import (  # noqa: F401
     ar_depth, attention, attention_rows, chunk_positions, gamma, history_ids_after,
     is_legal_order, key_latents, n_anchors, n_chunks, planner_blocks, planner_key_blocks, schedule,
 )
+from .block_causal import (  # noqa: F401
+    bc_backward, bc_complete_sources, bc_forward, bc_key_sources, bc_keys, bc_mask, source_rows,
+)
