@@ -1,6 +1,8 @@
 """Build the native libraries in-tree.
 
-  libff.so            C ABI + gfx950 HIP kernels (hipcc, --offload-arch=gfx950)
+  libff.so            C ABI + gfx950 HIP kernels (hipcc, --offload-arch=gfx950):
+                      ff_kernels.hip (renderer / planner attention, bank
+                      copies) and ff_bc_kernels.hip (block-causal backward)
   libff_hostcheck.so  the same host bookkeeping linked against a recording stub
                       instead of the kernels (g++); CPU tests use it to drive the
                       ABI's success paths without a GPU.
@@ -41,13 +43,17 @@ def build(verbose_resources: bool = False) -> None:
     host_obj = os.path.join(BUILD, "ff_host.o")
     _run(["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c", host_src, "-o", host_obj])
 
-    kern_src = os.path.join(CSRC, "hip", "ff_kernels.hip")
-    kern_obj = os.path.join(BUILD, "ff_kernels.o")
     extra = ["-Rpass-analysis=kernel-resource-usage"] if verbose_resources else []
-    _run([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS, *extra, *inc,
-          "-c", kern_src, "-o", kern_obj])
+    kern_objs = []
+    for name in ("ff_kernels", "ff_bc_kernels"):
+        src = os.path.join(CSRC, "hip", name + ".hip")
+        obj = os.path.join(BUILD, name + ".o")
+        _run([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS, *extra, *inc,
+              "-c", src, "-o", obj])
+        kern_objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", host_obj, kern_obj, "-o", tmp])
+    # -z defs: every symbol the host code calls must be defined by the kernels.
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", host_obj, *kern_objs, "-o", tmp])
     os.replace(tmp, LIB)
 
     stub_src = os.path.join(CSRC, "host", "device_stub.cpp")

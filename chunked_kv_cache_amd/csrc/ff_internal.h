@@ -83,12 +83,63 @@ struct CopyLaunch {
   int64_t block_stride;            // bytes between consecutive bank blocks
 };
 
+// Block-causal attention over a clip (training form).  Every source of the
+// clip has a fixed place in the workspace, so a chunk's key set is two index
+// ranges and the kernels need no per-chunk pointer table.
+constexpr int kBcMaxChunks = 96;
+constexpr int kBcMaxAnchors = 32;
+
+struct BcChunk {
+  int32_t a0, na;                  // anchors a0 .. a0+na-1 (Gamma(i), ascending)
+  int32_t j0, nj;                  // chunks j0 .. j0+nj-1; the last one is the chunk itself
+};
+
+struct BcReaders {
+  int32_t i0, n;                   // query chunks i0 .. i0+n-1 read this source
+};
+
+// Arguments of the backward kernels (by value, within the 4 KB limit).
+// Workspace blocks have the bank layout: part 0 = rows [nh][n][d], part 1 =
+// transposed [nh][d][n] of the pair named (kv = K rows + V^T, vk = V rows +
+// K^T, qq = Q rows + Q^T, gg = dO rows + dO^T).
+struct BcLaunch {
+  int32_t nh, d, T, L;             // heads, head dim, tokens per anchor / per chunk
+  int32_t n_anchor, n_chunk, dtype;
+  float scale;
+  int64_t blk_anchor, blk_chunk;   // bytes per anchor / chunk block
+  const uint8_t* kv_anchor;
+  const uint8_t* vk_anchor;
+  const uint8_t* kv_chunk;
+  const uint8_t* vk_chunk;
+  const uint8_t* qq_chunk;
+  const uint8_t* gg_chunk;
+  const void* Ka;                  // token-major inputs
+  const void* Va;
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;                // [N_c][nh][L], natural log
+  float* stats;                    // [N_c][nh][L][2]: -lse * log2(e), rowsum(dO * O)
+  void* dQ;                        // token-major outputs
+  void* dK;
+  void* dV;
+  void* dKa;
+  void* dVa;
+  BcChunk chunk[kBcMaxChunks];
+  BcReaders readers[kBcMaxAnchors + kBcMaxChunks];   // anchor a at [a], chunk j at [kBcMaxAnchors + j]
+};
+static_assert(sizeof(BcLaunch) <= 4096, "backward launch arguments exceed the kernel argument limit");
+
 // Device entry points.  Return 0 on success, FF_E_HIP on a launch error.
 // `prof` (nullable) collects start/stop events when profiling is on.
 struct Profiler;
 int dev_launch_attention(const AttnLaunch& a, void* stream, Profiler* prof);
 int dev_launch_publish(const CopyLaunch& c, void* stream, Profiler* prof, bool anchor);
 int dev_launch_unpack(const CopyLaunch& c, void* stream);
+int dev_launch_layout(const CopyLaunch& c, void* stream, Profiler* prof);    // block-causal operand copies
+int dev_launch_bc_backward(const BcLaunch& b, void* stream, Profiler* prof);
 Profiler* dev_profiler_create();
 void dev_profiler_destroy(Profiler* p);
 void dev_profiler_reset(Profiler* p);

@@ -13,7 +13,8 @@ struct Profiler {};
 namespace {
 AttnLaunch g_last_attn;
 CopyLaunch g_last_copy;
-int g_n_attn = 0, g_n_publish = 0, g_n_anchor = 0, g_n_unpack = 0;
+BcLaunch g_last_bc;
+int g_n_attn = 0, g_n_publish = 0, g_n_anchor = 0, g_n_unpack = 0, g_n_layout = 0, g_n_bc = 0;
 }  // namespace
 
 int dev_launch_attention(const AttnLaunch& a, void*, Profiler*) {
@@ -31,6 +32,18 @@ int dev_launch_publish(const CopyLaunch& c, void*, Profiler*, bool anchor) {
 int dev_launch_unpack(const CopyLaunch& c, void*) {
   g_last_copy = c;
   ++g_n_unpack;
+  return 0;
+}
+
+int dev_launch_layout(const CopyLaunch& c, void*, Profiler*) {
+  g_last_copy = c;
+  ++g_n_layout;
+  return 0;
+}
+
+int dev_launch_bc_backward(const BcLaunch& b, void*, Profiler*) {
+  g_last_bc = b;
+  ++g_n_bc;
   return 0;
 }
 
@@ -67,6 +80,29 @@ int ffstub_last_segments(int p, const void* ws, long long* offsets, int* n_token
 int ffstub_last_attn_pairs(int* n_wg) {
   *n_wg = ff::g_last_attn.n_wg;
   return ff::g_last_attn.n_pairs;
+}
+void ffstub_bc_counts(int* layout, int* backward) {
+  *layout = ff::g_n_layout;
+  *backward = ff::g_n_bc;
+}
+// Key ranges of chunk i and reader runs of source s (anchor a = s, chunk j =
+// s - n_anchor) of the last backward launch.
+void ffstub_last_bc_chunk(int i, int* a0, int* na, int* j0, int* nj) {
+  const ff::BcChunk& c = ff::g_last_bc.chunk[i];
+  *a0 = c.a0; *na = c.na; *j0 = c.j0; *nj = c.nj;
+}
+void ffstub_last_bc_readers(int s, int* i0, int* n) {
+  const int slot = s < ff::g_last_bc.n_anchor ? s : ff::kBcMaxAnchors + (s - ff::g_last_bc.n_anchor);
+  *i0 = ff::g_last_bc.readers[slot].i0;
+  *n = ff::g_last_bc.readers[slot].n;
+}
+// Number of jobs of the last copy launch and job j's source rows / block.
+int ffstub_last_copy_job(int j, const void** rows_k, const void** rows_v, int* nseg, int* L) {
+  *rows_k = ff::g_last_copy.job[j].rows_k;
+  *rows_v = ff::g_last_copy.job[j].rows_v;
+  *nseg = ff::g_last_copy.job[j].nseg;
+  *L = ff::g_last_copy.L;
+  return ff::g_last_copy.n_jobs;
 }
 // Destination block of job j of the last copy launch, as a byte offset from ws.
 long long ffstub_last_copy_block(int j, const void* ws) {

@@ -90,18 +90,48 @@ Layout layout_of(const ff_shape* s, int S, int H) {
 }
 
 // Gamma(i): reading of [S] "how it differs" / "how it is used" (see ff.h).
-int gamma_of(const ff_ctx* c, int i, int* ids) {
-  const int D = c->shape.anchor_stride, B = c->shape.chunk_latents;
+// The anchors come out ascending and consecutive under both rules.
+int gamma_ids(const ff_shape& s, int n_anchor, int i, int* ids) {
+  const int D = s.anchor_stride, B = s.chunk_latents;
   const int p0 = B * i, p1 = B * i + B - 1;
   int n = 0;
-  if (c->shape.gamma_rule == FF_GAMMA_BRACKET) {
+  if (s.gamma_rule == FF_GAMMA_BRACKET) {
     const int lo = (p0 / D) * D, hi = ((p1 + D - 1) / D) * D;
-    for (int a = lo / D; a <= hi / D && a < c->n_anchor; ++a) ids[n++] = a;
+    for (int a = lo / D; a <= hi / D && a < n_anchor; ++a) ids[n++] = a;
   } else {
     const int left = (p0 + B / 2) / D;
-    for (int a = left; a <= left + 1 && a < c->n_anchor; ++a) ids[n++] = a;
+    for (int a = left; a <= left + 1 && a < n_anchor; ++a) ids[n++] = a;
   }
   return n;
+}
+int gamma_of(const ff_ctx* c, int i, int* ids) { return gamma_ids(c->shape, c->n_anchor, i, ids); }
+
+// First history chunk of renderer chunk i when its bank holds chunks
+// [next - min(next, H), next): oldest dropped while the key latents exceed
+// W_ctx (reading of [S] "how it differs": W_ctx = 21).
+int history_first(const ff_shape& s, int H, int n_gamma, int i, int next) {
+  int h_first = next - std::min(next, H);
+  while (h_first < i && n_gamma + s.chunk_latents * (i - h_first + 1) > s.w_ctx) ++h_first;
+  return h_first;
+}
+
+// Key sources: n_gamma anchors, history chunks [h_first, i), then chunk i.
+void fill_render_plan(const int* ids, int na, int h_first, int i, int64_t T, int64_t Lq, int B,
+                      ff_key_sources* p) {
+  std::memset(p, 0, sizeof(*p));
+  int n = 0;
+  for (int j = 0; j < na; ++j) {
+    p->kind[n] = FF_SRC_ANCHOR; p->id[n] = ids[j]; p->n_tokens[n] = int32_t(T); ++n;
+  }
+  for (int ch = h_first; ch < i; ++ch) {
+    p->kind[n] = FF_SRC_HISTORY; p->id[n] = ch; p->n_tokens[n] = int32_t(Lq); ++n;
+  }
+  p->kind[n] = FF_SRC_OWN; p->id[n] = i; p->n_tokens[n] = int32_t(Lq); ++n;
+  p->n_sources = n;
+  p->key_latents = na + B * (i - h_first + 1);
+  int64_t tot = 0;
+  for (int j = 0; j < n; ++j) tot += p->n_tokens[j];
+  p->key_tokens = int32_t(tot);
 }
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -171,25 +201,10 @@ void plan_planner(const ff_ctx* c, int b, ff_key_sources* p) {
 // Key sources of (i, k): Gamma(i) anchors ascending, then B_k^(i) oldest
 // first, then the chunk itself; oldest history dropped while over W_ctx.
 void plan_of(const ff_ctx* c, int i, int k, ff_key_sources* p) {
-  std::memset(p, 0, sizeof(*p));
   int ids[8];
   const int na = gamma_of(c, i, ids);
-  const int B = c->shape.chunk_latents;
-  int h_first = c->next[k] - std::min(c->next[k], c->H);   // B_k^(i) = [h_first, i)
-  while (h_first < i && na + B * (i - h_first + 1) > c->shape.w_ctx) ++h_first;
-  int n = 0;
-  for (int j = 0; j < na; ++j) {
-    p->kind[n] = FF_SRC_ANCHOR; p->id[n] = ids[j]; p->n_tokens[n] = int32_t(c->T); ++n;
-  }
-  for (int ch = h_first; ch < i; ++ch) {
-    p->kind[n] = FF_SRC_HISTORY; p->id[n] = ch; p->n_tokens[n] = int32_t(c->Lq); ++n;
-  }
-  p->kind[n] = FF_SRC_OWN; p->id[n] = i; p->n_tokens[n] = int32_t(c->Lq); ++n;
-  p->n_sources = n;
-  p->key_latents = na + B * (i - h_first + 1);
-  int64_t tot = 0;
-  for (int j = 0; j < n; ++j) tot += p->n_tokens[j];
-  p->key_tokens = int32_t(tot);
+  const int h_first = history_first(c->shape, c->H, na, i, c->next[k]);   // B_k^(i) = [h_first, i)
+  fill_render_plan(ids, na, h_first, i, c->T, c->Lq, c->shape.chunk_latents, p);
 }
 
 // Device addresses of a call's sources.  k < 0 marks a planner call, whose
@@ -519,6 +534,327 @@ ff_status ff_profile_read(ff_ctx* c, ff_kernel_times* out) {
   std::memset(out, 0, sizeof(*out));
   if (!c->prof) return FF_OK;
   return dev_profiler_read(c->prof, out) == 0 ? FF_OK : FF_E_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Block-causal attention over a clip at one stage (training form).
+// [S] "how it works", training paragraph; reading: chunk i reads the keys of
+// ff_render_attend(i, k) with a full bank (see ff.h).
+// ---------------------------------------------------------------------------
+struct ff_bc {
+  ff_shape shape;
+  int H = 0;
+  int n_anchor = 0, n_chunk = 0;
+  int64_t T = 0, Lq = 0, esz = 2;
+  uint8_t* ws = nullptr;
+  // workspace regions (byte offsets from ws)
+  size_t blk_anchor = 0, blk_chunk = 0;
+  size_t kv_anchor = 0, vk_anchor = 0, kv_chunk = 0, vk_chunk = 0, qq_chunk = 0, gg_chunk = 0;
+  size_t stats = 0, part = 0, part_slot = 0;
+  std::vector<BcChunk> chunk;
+  std::vector<BcReaders> readers;      // anchors first, then chunks
+  Profiler* prof = nullptr;
+  bool profiling = false;
+};
+
+namespace {
+
+struct BcLayout {
+  size_t blk_anchor, blk_chunk, kv_anchor, vk_anchor, kv_chunk, vk_chunk, qq_chunk, gg_chunk;
+  size_t stats, part, part_slot, total;
+  int n_anchor, n_chunk;
+};
+
+bool bc_shape_ok(const ff_shape* s, int H) {
+  if (!shape_ok(s, 1, H)) return false;
+  const int n_anchor = (s->n_latents + s->anchor_stride - 1) / s->anchor_stride;
+  const int n_chunk = s->n_latents / s->chunk_latents;
+  return n_anchor <= kBcMaxAnchors && n_chunk <= kBcMaxChunks;
+}
+
+BcLayout bc_layout_of(const ff_shape* s) {
+  BcLayout L{};
+  const size_t esz = s->dtype == FF_F32 ? 4 : 2;
+  const size_t T = size_t(s->tokens_per_latent), nh = size_t(s->n_heads), d = size_t(s->head_dim);
+  const size_t lq = T * size_t(s->chunk_latents);
+  L.n_anchor = (s->n_latents + s->anchor_stride - 1) / s->anchor_stride;
+  L.n_chunk = s->n_latents / s->chunk_latents;
+  L.blk_anchor = align_up(2 * nh * T * d * esz);
+  L.blk_chunk = align_up(2 * nh * lq * d * esz);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += align_up(bytes); return o; };
+  L.kv_anchor = take(size_t(L.n_anchor) * L.blk_anchor);
+  L.vk_anchor = take(size_t(L.n_anchor) * L.blk_anchor);
+  L.kv_chunk = take(size_t(L.n_chunk) * L.blk_chunk);
+  L.vk_chunk = take(size_t(L.n_chunk) * L.blk_chunk);
+  L.qq_chunk = take(size_t(L.n_chunk) * L.blk_chunk);
+  L.gg_chunk = take(size_t(L.n_chunk) * L.blk_chunk);
+  L.stats = take(size_t(L.n_chunk) * nh * lq * 8);
+  L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(kBlockM) * (d + 2) * 4) : 0;
+  L.part = take(size_t(kMaxPairs) * size_t(kCUs) * 2 * L.part_slot);
+  L.total = off;
+  return L;
+}
+
+// Key ranges of every chunk and, transposed, the chunks that read each source.
+void bc_plan(ff_bc* b) {
+  b->chunk.assign(size_t(b->n_chunk), BcChunk{});
+  for (int i = 0; i < b->n_chunk; ++i) {
+    int ids[8];
+    const int na = gamma_ids(b->shape, b->n_anchor, i, ids);
+    const int h_first = history_first(b->shape, b->H, na, i, i);
+    b->chunk[size_t(i)] = BcChunk{na ? ids[0] : 0, na, h_first, i - h_first + 1};
+  }
+  // The readers of a source form one run of consecutive chunks: Gamma's
+  // anchors and the history start never move backwards as i grows.
+  b->readers.assign(size_t(b->n_anchor + b->n_chunk), BcReaders{0, 0});
+  for (int i = 0; i < b->n_chunk; ++i) {
+    const BcChunk& c = b->chunk[size_t(i)];
+    auto add = [&](int src) {
+      BcReaders& r = b->readers[size_t(src)];
+      if (r.n == 0) r.i0 = i;
+      r.n = i - r.i0 + 1;
+    };
+    for (int a = c.a0; a < c.a0 + c.na; ++a) add(a);
+    for (int j = c.j0; j < c.j0 + c.nj; ++j) add(b->n_anchor + j);
+  }
+}
+
+bool bc_reads(const ff_bc* b, int i, int src) {
+  const BcChunk& c = b->chunk[size_t(i)];
+  if (src < b->n_anchor) return src >= c.a0 && src < c.a0 + c.na;
+  const int j = src - b->n_anchor;
+  return j >= c.j0 && j < c.j0 + c.nj;
+}
+
+CopyLaunch bc_copy(const ff_bc* b, int64_t L, int64_t block_stride) {
+  CopyLaunch cl;
+  std::memset(&cl, 0, sizeof(cl));
+  cl.L = int32_t(L);
+  cl.nh = b->shape.n_heads;
+  cl.d = b->shape.head_dim;
+  cl.dtype = b->shape.dtype;
+  cl.block_stride = block_stride;
+  return cl;
+}
+
+void bc_add_job(CopyLaunch* cl, const void* rows_k, const void* rows_v, uint8_t* block, int nseg) {
+  CopyJob& j = cl->job[cl->n_jobs++];
+  j.rows_k = rows_k;
+  j.rows_v = rows_v;
+  j.block = block;
+  j.nseg = nseg;
+  cl->max_nseg = std::max(cl->max_nseg, nseg);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ff_bc_workspace_bytes(const ff_shape* shape, int history) {
+  if (!bc_shape_ok(shape, history)) return 0;
+  return bc_layout_of(shape).total;
+}
+
+ff_status ff_bc_create(const ff_shape* shape, int history, void* workspace, size_t workspace_bytes, ff_bc** out) {
+  if (!out) return FF_E_INVAL;
+  *out = nullptr;
+  if (!bc_shape_ok(shape, history)) return FF_E_INVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))) return FF_E_INVAL;
+  const BcLayout L = bc_layout_of(shape);
+  if (workspace_bytes < L.total) return FF_E_NOSPACE;
+  ff_bc* b = new (std::nothrow) ff_bc();
+  if (!b) return FF_E_INVAL;
+  b->shape = *shape;
+  b->H = history;
+  b->n_anchor = L.n_anchor;
+  b->n_chunk = L.n_chunk;
+  b->T = shape->tokens_per_latent;
+  b->Lq = int64_t(shape->tokens_per_latent) * shape->chunk_latents;
+  b->esz = elem_size(shape->dtype);
+  b->ws = static_cast<uint8_t*>(workspace);
+  b->blk_anchor = L.blk_anchor;
+  b->blk_chunk = L.blk_chunk;
+  b->kv_anchor = L.kv_anchor;
+  b->vk_anchor = L.vk_anchor;
+  b->kv_chunk = L.kv_chunk;
+  b->vk_chunk = L.vk_chunk;
+  b->qq_chunk = L.qq_chunk;
+  b->gg_chunk = L.gg_chunk;
+  b->stats = L.stats;
+  b->part = L.part;
+  b->part_slot = L.part_slot;
+  bc_plan(b);
+  for (int src = 0; src < b->n_anchor + b->n_chunk; ++src)      // one run per source
+    for (int i = 0; i < b->n_chunk; ++i) {
+      const BcReaders& r = b->readers[size_t(src)];
+      if (bc_reads(b, i, src) != (r.n > 0 && i >= r.i0 && i < r.i0 + r.n)) {
+        delete b;
+        return FF_E_INVAL;
+      }
+    }
+  *out = b;
+  return FF_OK;
+}
+
+void ff_bc_destroy(ff_bc* b) {
+  if (!b) return;
+  if (b->prof) dev_profiler_destroy(b->prof);
+  delete b;
+}
+
+ff_status ff_bc_key_plan(const ff_bc* b, int chunk, ff_key_sources* out) {
+  if (!b || !out) return FF_E_INVAL;
+  if (chunk < 0 || chunk >= b->n_chunk) return FF_E_RANGE;
+  const BcChunk& c = b->chunk[size_t(chunk)];
+  int ids[8];
+  for (int j = 0; j < c.na; ++j) ids[j] = c.a0 + j;
+  fill_render_plan(ids, c.na, c.j0, chunk, b->T, b->Lq, b->shape.chunk_latents, out);
+  return FF_OK;
+}
+
+ff_status ff_bc_forward(ff_bc* b, const void* Ka, const void* Va, const void* Q, const void* K, const void* V,
+                        void* O, float* lse, void* stream) {
+  if (!b || !aligned16(Ka) || !aligned16(Va) || !aligned16(Q) || !aligned16(K) || !aligned16(V) ||
+      !aligned16(O) || !lse_ok(lse))
+    return FF_E_INVAL;
+  Profiler* prof = b->profiling ? b->prof : nullptr;
+  // 1) Operand copies in bank layout: K rows + V^T of every anchor and chunk.
+  CopyLaunch ca = bc_copy(b, b->T, int64_t(b->blk_anchor));
+  bc_add_job(&ca, Ka, Va, b->ws + b->kv_anchor, b->n_anchor);
+  if (dev_launch_layout(ca, stream, prof) != 0) return FF_E_HIP;
+  CopyLaunch cc = bc_copy(b, b->Lq, int64_t(b->blk_chunk));
+  bc_add_job(&cc, K, V, b->ws + b->kv_chunk, b->n_chunk);
+  if (dev_launch_layout(cc, stream, prof) != 0) return FF_E_HIP;
+
+  // 2) The segmented attention kernel, up to kMaxPairs chunks per launch.
+  const int64_t row_bytes = b->Lq * b->shape.n_heads * b->shape.head_dim * b->esz;
+  for (int i0 = 0; i0 < b->n_chunk; i0 += kMaxPairs) {
+    const int n = std::min(kMaxPairs, b->n_chunk - i0);
+    AttnLaunch a;
+    std::memset(&a, 0, sizeof(a));
+    a.n_pairs = n;
+    a.nh = b->shape.n_heads;
+    a.d = b->shape.head_dim;
+    a.lq = int32_t(b->Lq);
+    a.n_qtiles = int32_t((b->Lq + kBlockM - 1) / kBlockM);
+    a.n_wg = kCUs;
+    a.dtype = b->shape.dtype;
+    a.scale = float(1.0 / std::sqrt(double(b->shape.head_dim)));
+    a.slot_floats = int64_t(b->part_slot / 4);
+    for (int p = 0; p < n; ++p) {
+      const int i = i0 + p;
+      const BcChunk& c = b->chunk[size_t(i)];
+      PairLaunch& pl = a.pair[p];
+      pl.q = static_cast<const uint8_t*>(Q) + i * row_bytes;
+      pl.o = static_cast<uint8_t*>(O) + i * row_bytes;
+      pl.lse = lse ? lse + int64_t(i) * b->shape.n_heads * b->Lq : nullptr;
+      SegTable& t = pl.seg;
+      int32_t tiles = 0, s = 0;
+      auto add = [&](const uint8_t* base, int64_t ntok) {
+        t.base[s] = base;
+        t.n[s] = int32_t(ntok);
+        t.tile_start[s] = tiles;
+        tiles += int32_t((ntok + kBlockN - 1) / kBlockN);
+        ++s;
+      };
+      for (int x = c.a0; x < c.a0 + c.na; ++x) add(b->ws + b->kv_anchor + size_t(x) * b->blk_anchor, b->T);
+      for (int j = c.j0; j < c.j0 + c.nj; ++j) add(b->ws + b->kv_chunk + size_t(j) * b->blk_chunk, b->Lq);
+      t.tile_start[s] = tiles;
+      t.nseg = s;
+      pl.lk = int32_t(int64_t(c.na) * b->T + int64_t(c.nj) * b->Lq);
+      pl.ntiles = tiles;
+      pl.n_items = a.nh * a.n_qtiles;
+      pl.part = b->part_slot ? reinterpret_cast<float*>(b->ws + b->part + size_t(p) * size_t(kCUs) * 2 * b->part_slot)
+                             : nullptr;
+    }
+    if (dev_launch_attention(a, stream, prof) != 0) return FF_E_HIP;
+  }
+  return FF_OK;
+}
+
+ff_status ff_bc_backward(ff_bc* b, const void* Ka, const void* Va, const void* Q, const void* K, const void* V,
+                         const void* O, const float* lse, const void* dO, void* dQ, void* dK, void* dV, void* dKa,
+                         void* dVa, void* stream) {
+  if (!b || !aligned16(Ka) || !aligned16(Va) || !aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) ||
+      !lse || !lse_ok(lse) || !aligned16(dO) || !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) ||
+      !aligned16(dKa) || !aligned16(dVa))
+    return FF_E_INVAL;
+  Profiler* prof = b->profiling ? b->prof : nullptr;
+  // 1) Operand copies (bf16 MFMA path only; the f32 path reads rows directly).
+  if (b->shape.dtype == FF_BF16) {
+    CopyLaunch ca = bc_copy(b, b->T, int64_t(b->blk_anchor));
+    bc_add_job(&ca, Ka, Va, b->ws + b->kv_anchor, b->n_anchor);
+    bc_add_job(&ca, Va, Ka, b->ws + b->vk_anchor, b->n_anchor);
+    if (dev_launch_layout(ca, stream, prof) != 0) return FF_E_HIP;
+    CopyLaunch cc = bc_copy(b, b->Lq, int64_t(b->blk_chunk));
+    bc_add_job(&cc, K, V, b->ws + b->kv_chunk, b->n_chunk);
+    bc_add_job(&cc, V, K, b->ws + b->vk_chunk, b->n_chunk);
+    bc_add_job(&cc, Q, Q, b->ws + b->qq_chunk, b->n_chunk);
+    bc_add_job(&cc, dO, dO, b->ws + b->gg_chunk, b->n_chunk);
+    if (dev_launch_layout(cc, stream, prof) != 0) return FF_E_HIP;
+  }
+  // 2) rowsum(dO * O), then dQ and dK/dV.
+  BcLaunch bl;
+  std::memset(&bl, 0, sizeof(bl));
+  bl.nh = b->shape.n_heads;
+  bl.d = b->shape.head_dim;
+  bl.T = int32_t(b->T);
+  bl.L = int32_t(b->Lq);
+  bl.n_anchor = b->n_anchor;
+  bl.n_chunk = b->n_chunk;
+  bl.dtype = b->shape.dtype;
+  bl.scale = float(1.0 / std::sqrt(double(b->shape.head_dim)));
+  bl.blk_anchor = int64_t(b->blk_anchor);
+  bl.blk_chunk = int64_t(b->blk_chunk);
+  bl.kv_anchor = b->ws + b->kv_anchor;
+  bl.vk_anchor = b->ws + b->vk_anchor;
+  bl.kv_chunk = b->ws + b->kv_chunk;
+  bl.vk_chunk = b->ws + b->vk_chunk;
+  bl.qq_chunk = b->ws + b->qq_chunk;
+  bl.gg_chunk = b->ws + b->gg_chunk;
+  bl.Ka = Ka;
+  bl.Va = Va;
+  bl.Q = Q;
+  bl.K = K;
+  bl.V = V;
+  bl.O = O;
+  bl.dO = dO;
+  bl.lse = lse;
+  bl.stats = reinterpret_cast<float*>(b->ws + b->stats);
+  bl.dQ = dQ;
+  bl.dK = dK;
+  bl.dV = dV;
+  bl.dKa = dKa;
+  bl.dVa = dVa;
+  for (int i = 0; i < b->n_chunk; ++i) bl.chunk[i] = b->chunk[size_t(i)];
+  for (int s = 0; s < b->n_anchor + b->n_chunk; ++s) {
+    // anchors at [0, n_anchor), chunks at kBcMaxAnchors + j
+    const int slot = s < b->n_anchor ? s : kBcMaxAnchors + (s - b->n_anchor);
+    bl.readers[slot] = b->readers[size_t(s)];
+  }
+  if (dev_launch_bc_backward(bl, stream, prof) != 0) return FF_E_HIP;
+  return FF_OK;
+}
+
+ff_status ff_bc_profile_enable(ff_bc* b, int on) {
+  if (!b) return FF_E_INVAL;
+  if (on && !b->prof) {
+    b->prof = dev_profiler_create();
+    if (!b->prof) return FF_E_HIP;
+  }
+  if (b->prof) dev_profiler_reset(b->prof);
+  b->profiling = on != 0;
+  return FF_OK;
+}
+
+ff_status ff_bc_profile_read(ff_bc* b, ff_kernel_times* out) {
+  if (!b || !out) return FF_E_INVAL;
+  std::memset(out, 0, sizeof(*out));
+  if (!b->prof) return FF_OK;
+  return dev_profiler_read(b->prof, out) == 0 ? FF_OK : FF_E_HIP;
 }
 
 }  // extern "C"

@@ -43,7 +43,11 @@ class ff_kernel_times(ctypes.Structure):
     _fields_ = [("attn_launches", ctypes.c_int64), ("attn_ms", ctypes.c_double),
                 ("merge_launches", ctypes.c_int64), ("merge_ms", ctypes.c_double),
                 ("publish_launches", ctypes.c_int64), ("publish_ms", ctypes.c_double),
-                ("anchor_launches", ctypes.c_int64), ("anchor_ms", ctypes.c_double)]
+                ("anchor_launches", ctypes.c_int64), ("anchor_ms", ctypes.c_double),
+                ("layout_launches", ctypes.c_int64), ("layout_ms", ctypes.c_double),
+                ("bwd_pre_launches", ctypes.c_int64), ("bwd_pre_ms", ctypes.c_double),
+                ("bwd_dq_launches", ctypes.c_int64), ("bwd_dq_ms", ctypes.c_double),
+                ("bwd_dkv_launches", ctypes.c_int64), ("bwd_dkv_ms", ctypes.c_double)]
 
 
 class FFError(RuntimeError):
@@ -72,6 +76,14 @@ _SIGS = {
     "ff_stage_bank_rewind": (_I, [_VP, _I]),
     "ff_profile_enable": (_I, [_VP, _I]),
     "ff_profile_read": (_I, [_VP, ctypes.POINTER(ff_kernel_times)]),
+    "ff_bc_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ff_shape), _I]),
+    "ff_bc_create": (_I, [ctypes.POINTER(ff_shape), _I, _VP, ctypes.c_size_t, ctypes.POINTER(_VP)]),
+    "ff_bc_destroy": (None, [_VP]),
+    "ff_bc_forward": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "ff_bc_backward": (_I, [_VP] + [_VP] * 14),
+    "ff_bc_key_plan": (_I, [_VP, _I, ctypes.POINTER(ff_key_sources)]),
+    "ff_bc_profile_enable": (_I, [_VP, _I]),
+    "ff_bc_profile_read": (_I, [_VP, ctypes.POINTER(ff_kernel_times)]),
     "ff_status_str": (ctypes.c_char_p, [_I]),
 }
 SYMBOLS = tuple(_SIGS)
@@ -243,6 +255,81 @@ class StageBanks:
     def close(self):
         if getattr(self, "ctx", None):
             ff_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------------------
+# Block-causal attention over a clip (training form)
+# ---------------------------------------------------------------------------
+def ff_bc_workspace_bytes(shape: ff_shape, history: int, L=None) -> int:
+    L = L or lib()
+    return int(L.ff_bc_workspace_bytes(ctypes.byref(shape), history))
+
+
+def ff_bc_create(shape: ff_shape, history: int, workspace, workspace_bytes: int, L=None) -> int:
+    L = L or lib()
+    out = _VP()
+    _check(L.ff_bc_create(ctypes.byref(shape), history, _ptr(workspace), workspace_bytes, ctypes.byref(out)), L)
+    return out.value
+
+
+def ff_bc_destroy(bc, L=None) -> None:
+    L = L or lib()
+    L.ff_bc_destroy(bc)
+
+
+def ff_bc_forward(bc, Ka, Va, Q, K, V, O, lse=None, stream=None, L=None) -> None:
+    L = L or lib()
+    _check(L.ff_bc_forward(bc, _ptr(Ka), _ptr(Va), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
+                           _stream(stream, Q, O)), L)
+
+
+def ff_bc_backward(bc, Ka, Va, Q, K, V, O, lse, dO, dQ, dK, dV, dKa, dVa, stream=None, L=None) -> None:
+    L = L or lib()
+    _check(L.ff_bc_backward(bc, _ptr(Ka), _ptr(Va), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse), _ptr(dO),
+                            _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dKa), _ptr(dVa), _stream(stream, Q, dQ)), L)
+
+
+def ff_bc_key_plan(bc, chunk, L=None) -> ff_key_sources:
+    L = L or lib()
+    out = ff_key_sources()
+    _check(L.ff_bc_key_plan(bc, chunk, ctypes.byref(out)), L)
+    return out
+
+
+def ff_bc_profile_enable(bc, on: bool, L=None) -> None:
+    L = L or lib()
+    _check(L.ff_bc_profile_enable(bc, 1 if on else 0), L)
+
+
+def ff_bc_profile_read(bc, L=None) -> dict:
+    L = L or lib()
+    t = ff_kernel_times()
+    _check(L.ff_bc_profile_read(bc, ctypes.byref(t)), L)
+    return {f: getattr(t, f) for f, _ in ff_kernel_times._fields_}
+
+
+class BlockCausal:
+    """Owns one block-causal context and its torch-allocated workspace."""
+
+    def __init__(self, shape: ff_shape, history: int, device="cuda"):
+        import torch
+        self.shape, self.history = shape, history
+        self.ws_bytes = ff_bc_workspace_bytes(shape, history)
+        if self.ws_bytes == 0:
+            raise FFError(FF_E_INVAL, "unsupported shape")
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.ctx = ff_bc_create(shape, history, self.workspace, self.ws_bytes)
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            ff_bc_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):

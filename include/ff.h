@@ -106,6 +106,10 @@ typedef struct {
   int64_t merge_launches;   double merge_ms;     /* split-K LSE merge          */
   int64_t publish_launches; double publish_ms;   /* Tail_H stage-bank publish  */
   int64_t anchor_launches;  double anchor_ms;    /* anchor-bank publish        */
+  int64_t layout_launches;  double layout_ms;    /* block-causal operand copies */
+  int64_t bwd_pre_launches; double bwd_pre_ms;   /* rowsum(dO*O), -lse*log2(e)  */
+  int64_t bwd_dq_launches;  double bwd_dq_ms;    /* dQ (query-major)           */
+  int64_t bwd_dkv_launches; double bwd_dkv_ms;   /* dK, dV (key-major)         */
 } ff_kernel_times;
 
 /* Bytes of device workspace for a context with n_stages banks of history H.
@@ -217,6 +221,60 @@ ff_status ff_plan_key_plan(const ff_ctx* ctx, int block, ff_key_sources* out);
  * the accumulated totals since enabling (enable also resets them).            */
 ff_status ff_profile_enable(ff_ctx* ctx, int on);
 ff_status ff_profile_read(ff_ctx* ctx, ff_kernel_times* out);
+
+/* ---------------------------------------------------------------------------
+ * Block-causal renderer attention over a whole clip at one stage: the
+ * training form of the renderer attention, forward and backward.
+ * [S] "how it works", training paragraph: a renderer target attends the clean
+ * anchor KV that Gamma(i) allows and the previous H chunks at its own noise
+ * level; in self-rollout distillation the renderer runs as one block-causal
+ * forward over the clip instead of per-chunk cache updates, so that gradients
+ * reach earlier chunks from later ones and the planner (through the anchors)
+ * from the renderer.
+ * Reading taken (not printed on the pages): chunk i's queries attend exactly
+ * the keys ff_render_attend(i, k) reads once its bank is full -- the anchors
+ * of Gamma(i), chunks max(0, i-H) .. i-1 (oldest dropped first while the key
+ * latents exceed W_ctx) and chunk i itself, no mask inside a source -- so
+ * chunk i's output equals that call's output on the same K/V.
+ *
+ * Tensors (token-major, context dtype, 16-byte aligned, caller-owned):
+ *   Ka, Va, dKa, dVa   [N_a*T][n_heads][head_dim], anchor a at rows a*T ..
+ *   Q, K, V, O, dO,
+ *   dQ, dK, dV         [N_c*B_R*T][n_heads][head_dim], chunk i at rows i*B_R*T ..
+ *   lse                f32 [N_c][n_heads][B_R*T], natural log
+ * with N_a = ceil(n_latents / Delta) and N_c = n_latents / B_R.  The
+ * workspace holds the operand copies in bank layout; it is scratch between
+ * calls (no state is kept in it from one call to the next).  Limits:
+ * N_c <= 96, N_a <= 32.  Same validation / stream / error conventions as the
+ * calls above; the gradients are written, not accumulated.                   */
+typedef struct ff_bc ff_bc;
+
+/* Workspace bytes of a block-causal context (0 if the shape is unsupported). */
+size_t ff_bc_workspace_bytes(const ff_shape* shape, int history);
+ff_status ff_bc_create(const ff_shape* shape, int history, void* workspace, size_t workspace_bytes,
+                       ff_bc** out);
+void ff_bc_destroy(ff_bc* bc);
+
+/* ff_bc_forward -- O and lse of every chunk (lse may be NULL). */
+ff_status ff_bc_forward(ff_bc* bc, const void* Ka, const void* Va, const void* Q, const void* K,
+                        const void* V, void* O, float* lse, void* stream);
+
+/* ff_bc_backward -- gradients of sum(dO * O) with respect to Q, K, V and the
+ * anchors' K, V, given the inputs, the forward's O and lse, and dO.  Every
+ * pointer is required.  dK/dV of a chunk sum the contributions of the (up to
+ * H+1) chunks that read it; dKa/dVa of an anchor those of the chunks whose
+ * Gamma holds it.                                                            */
+ff_status ff_bc_backward(ff_bc* bc, const void* Ka, const void* Va, const void* Q, const void* K,
+                         const void* V, const void* O, const float* lse, const void* dO,
+                         void* dQ, void* dK, void* dV, void* dKa, void* dVa, void* stream);
+
+/* ff_bc_key_plan -- chunk i's key sources (FF_SRC_ANCHOR, FF_SRC_HISTORY,
+ * FF_SRC_OWN) as ff_bc_forward reads them.  Host only.                       */
+ff_status ff_bc_key_plan(const ff_bc* bc, int chunk, ff_key_sources* out);
+
+/* Per-kernel device timing of a block-causal context (as ff_profile_*). */
+ff_status ff_bc_profile_enable(ff_bc* bc, int on);
+ff_status ff_bc_profile_read(ff_bc* bc, ff_kernel_times* out);
 
 /* Static description of a status code. */
 const char* ff_status_str(ff_status s);

@@ -15,7 +15,7 @@ kind   : 0 = renderer chunk input, 1 = anchor (planner cache-extraction output),
          2 = planner block input during its denoising steps
 idx    : chunk id for kind 0, anchor id for kind 1, planner block for kind 2
 stage  : denoising stage for kind 0, always 0 for kind 1, step for kind 2
-tensor : 0 = Q, 1 = K, 2 = V
+tensor : 0 = Q, 1 = K, 2 = V, 3 = dO (output gradient of a backward pass)
 
 Every tensor is token-major ``[tokens, n_heads, head_dim]``.
 bf16 tensors are returned as ``uint16`` bit patterns; ``bf16_bits_to_f32``
@@ -28,7 +28,7 @@ import numpy as np
 KIND_RENDER = 0
 KIND_ANCHOR = 1
 KIND_PLANNER = 2
-TENSOR_Q, TENSOR_K, TENSOR_V = 0, 1, 2
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_DO = 0, 1, 2, 3
 
 
 def _stream(seed: int, kind: int, layer: int, idx: int, stage: int, tensor: int) -> np.random.Generator:
@@ -101,3 +101,24 @@ def planner_qkv(*, T: int, n_heads: int, head_dim: int, block: int, step: int, n
     k = normal_tensor(shape, tensor=TENSOR_K, **kw)
     v = normal_tensor(shape, tensor=TENSOR_V, **kw)
     return q, k, v
+
+
+def clip_tensors(*, T: int, n_heads: int, head_dim: int, n_chunks: int, stage: int = 0, seed: int = 0,
+                 layer: int = 0, chunk_latents: int = 3, dtype: str = "bf16", q_scale: float = 1.0,
+                 chunks=None):
+    """Q, K, V, dO of a whole clip at one stage, chunk after chunk: each [n_chunks*chunk_latents*T, nh, d].
+
+    Chunk i's Q, K, V are the renderer inputs of (chunk i, stage) (kind 0), so
+    the clip equals the per-chunk inputs laid end to end; dO is tensor 3 of
+    the same stream family.  ``chunks`` limits generation to those chunks (the
+    other rows are zero).
+    """
+    L = chunk_latents * T
+    shape = (L, n_heads, head_dim)
+    out_dtype = np.uint16 if dtype == "bf16" else np.float32
+    out = [np.zeros((n_chunks * L, n_heads, head_dim), dtype=out_dtype) for _ in range(4)]
+    for i in (range(n_chunks) if chunks is None else chunks):
+        kw = dict(seed=seed, kind=KIND_RENDER, layer=layer, idx=int(i), stage=stage, dtype=dtype)
+        for t, (dst, scale) in enumerate(zip(out, (q_scale, 1.0, 1.0, 1.0))):
+            dst[i * L:(i + 1) * L] = normal_tensor(shape, tensor=t, scale=scale, **kw)
+    return tuple(out)
