@@ -56,6 +56,9 @@ WORKLOADS = {
     # planner role: block 8 of a 261-latent clip (27 anchors, 9 blocks of 3)
     "plan480": (1560, 12, 8, 261, 1, "480p planner block step: block 8 of 261 latents, 4680 queries x 32760 "
                                      "keys (18 anchors of 6 earlier blocks + own 3 latents), 12 heads x 128"),
+    # block-causal training form: forward + backward of one stage over a whole clip
+    "bc480": (1560, 12, 0, 81, 1, "480p block-causal training pass: forward + backward of one stage over the "
+                                  "81-latent clip (27 chunks of 4680 queries, 9 anchors), 12 heads x 128"),
 }
 
 
@@ -63,12 +66,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload):
-    """HBM bytes per attention dispatch from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary, or None when the kernel source changed since."""
+def measured_traffic(workload, kernel="attn", source="ff_kernels.hip"):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when the kernel source changed since."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"attn_{workload}_traffic.md")
-    src = os.path.join(ROOT, "chunked_kv_cache_amd", "csrc", "hip", "ff_kernels.hip")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    src = os.path.join(ROOT, "chunked_kv_cache_amd", "csrc", "hip", source)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -107,6 +110,8 @@ def main():
 
     if args.workload.startswith("plan"):
         return run_planner(args)
+    if args.workload.startswith("bc"):
+        return run_block_causal(args)
     if args.workload.startswith("rollout"):
         return run_rollout(args)
     T, nh, chunk, n_latents, S, desc = WORKLOADS[args.workload]
@@ -421,6 +426,130 @@ def run_planner(args):
     }
     print(json.dumps(res), flush=True)
     banks.close()
+
+
+def run_block_causal(args):
+    """Block-causal training form: one step = ff_bc_forward + ff_bc_backward of
+    one stage over the whole clip (operand copies, the segmented attention
+    over every chunk's key set, row statistics, dQ and dK/dV kernels)."""
+    import torch
+
+    import oracle as orc
+    from chunked_kv_cache_amd import ff
+
+    T, nh, _, n_latents, _, desc = WORKLOADS[args.workload]
+    d, H = 128, 5
+    torch.cuda.set_device(0)
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=nh, head_dim=d, n_latents=n_latents, history=H)
+    nc, na, L = orc.n_chunks(cfg), orc.n_anchors(cfg), cfg.chunk_tokens
+    bc = ff.BlockCausal(ff.make_shape(n_heads=nh, head_dim=d, tokens_per_latent=T, n_latents=n_latents), H)
+    t0 = time.time()
+    # Seeded N(0,1) bf16 drawn on the device (the clip is 1.6 GB of inputs).
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    rnd = lambda rows: torch.randn((rows, nh, d), generator=gen, device="cuda").to(torch.bfloat16)
+    Ka, Va = rnd(na * T), rnd(na * T)
+    Q, K, V, dO = rnd(nc * L), rnd(nc * L), rnd(nc * L), rnd(nc * L)
+    O = torch.empty_like(Q)
+    lse = torch.empty((nc, nh, L), dtype=torch.float32, device="cuda")
+    dQ, dK, dV, dKa, dVa = (torch.empty_like(x) for x in (Q, K, V, Ka, Va))
+    keys = [ff.ff_bc_key_plan(bc.ctx, i).key_tokens for i in range(nc)]
+    pair_flops = float(sum(L * lk for lk in keys)) * d * nh          # sum of Lq*Lk*d*nh
+    fwd_flops, bwd_flops = 4.0 * pair_flops, 10.0 * pair_flops         # backward = 2.5 x forward
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t0:.1f}s; {fwd_flops / 1e12:.2f} TFLOP forward, {bwd_flops / 1e12:.2f} backward")
+
+    def step():
+        ff.ff_bc_forward(bc.ctx, Ka, Va, Q, K, V, O, lse, stream=stream)
+        ff.ff_bc_backward(bc.ctx, Ka, Va, Q, K, V, O, lse, dO, dQ, dK, dV, dKa, dVa, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ff.ff_bc_profile_enable(bc.ctx, True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    prof = ff.ff_bc_profile_read(bc.ctx)
+    ff.ff_bc_profile_enable(bc.ctx, False)
+    ms_per_step = wall * 1e3 / args.steps
+    tflops = (fwd_flops + bwd_flops) * args.steps / wall / 1e12
+    per = lambda k: prof[f"{k}_ms"] / args.steps                     # ms per step of a kernel family
+    kern = {"attention": (per("attn"), fwd_flops), "dq": (per("bwd_dq"), 6.0 * pair_flops),
+            "dkv": (per("bwd_dkv"), 8.0 * pair_flops)}
+    for k, (ms, fl) in kern.items():
+        log(f"{k}: {ms:.2f} ms per step, {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    log(f"merge {per('merge'):.3f} ms, copies {per('layout'):.3f} ms, row statistics {per('bwd_pre'):.3f} ms; "
+        f"step {ms_per_step:.2f} ms")
+    dom = max(kern, key=lambda k: kern[k][0])
+    dom_ms, dom_flops = kern[dom]
+    launches = {"attention": prof["attn_launches"], "dq": prof["bwd_dq_launches"],
+                "dkv": prof["bwd_dkv_launches"]}[dom] / args.steps
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    if args.calibration_copy:
+        calibration_copy()
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_block_causal(T, nh, d, n_latents, H, 1)
+    src = "ff_kernels.hip" if dom == "attention" else "ff_bc_kernels.hip"
+    tag = {"attention": "attn", "dq": "bc_dq", "dkv": "bc_dkv"}[dom]
+    res = {
+        "metric": "block-causal training attention TFLOP/s (forward + backward, % bf16 MFMA peak)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO and anchors drawn on the device, 480p clip shapes)",
+        "config": {"workload": desc, "chunks": nc, "anchors": na, "queries_per_chunk": L, "heads": nh,
+                   "head_dim": d, "history": H, "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "forward_tflops": round(fwd_flops / (sum(per(k) for k in ("layout", "attn", "merge")) * 1e-3) / 1e12, 1),
+        "kernel_ms_per_step": {k: round(v[0], 3) for k, v in kern.items()} |
+                              {"merge": round(per("merge"), 3), "copies": round(per("layout"), 3),
+                               "row_statistics": round(per("bwd_pre"), 3)},
+        "roofline": {"bound": "mfma", "kernel": tag, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload, tag, src)},
+        "cpu_baseline": cpu,
+    }
+    if launches != 1:
+        res["roofline"]["launches_per_step"] = launches
+    print(json.dumps(res), flush=True)
+    bc.close()
+
+
+def cpu_baseline_block_causal(T, nh, d, n_latents, H, n_heads_sample, chunk=5):
+    """The float64 oracle's block-causal forward and backward restricted to
+    the query rows of one steady-state chunk, on `n_heads_sample` heads."""
+    import oracle as orc
+    import synthetic as syn
+    threads = _threads()
+    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=n_heads_sample, head_dim=d, n_latents=n_latents, history=H)
+    nc, na = orc.n_chunks(cfg), orc.n_anchors(cfg)
+    srcs = orc.bc_key_sources(cfg, chunk)
+    need = [j for k, j in srcs if k == "chunk"]
+    hs = slice(0, n_heads_sample)
+    Ka, Va = (syn.as_f64(x, "bf16")[:, hs] for x in syn.anchor_kv(T=T, n_heads=nh, head_dim=d, anchors=range(na)))
+    Q, K, V, dO = (syn.as_f64(x, "bf16")[:, hs]
+                   for x in syn.clip_tensors(T=T, n_heads=nh, head_dim=d, n_chunks=nc, chunks=need))
+    t0 = time.perf_counter()
+    orc.bc_forward(cfg, Ka, Va, Q, K, V, chunks=[chunk])
+    orc.bc_backward(cfg, Ka, Va, Q, K, V, dO, chunks=[chunk])
+    dt = time.perf_counter() - t0
+    n_keys = sum(T if k == "anchor" else 3 * T for k, _ in srcs)
+    flops = 14.0 * 3 * T * n_keys * d * n_heads_sample
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle block-causal forward + backward for the queries of chunk {chunk} "
+                      f"({n_keys} keys), {n_heads_sample} of {nh} heads: {flops / 1e9:.0f} GFLOP in {dt:.1f} s"}
 
 
 def cpu_baseline_planner(host_qkv, block, T, nh, d, n_heads_sample, n_latents):
