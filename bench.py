@@ -479,7 +479,7 @@ def run_block_causal(args):
     tflops = (fwd_flops + bwd_flops) * args.steps / wall / 1e12
     per = lambda k: prof[f"{k}_ms"] / args.steps                     # ms per step of a kernel family
     kern = {"attention": (per("attn"), fwd_flops), "dq": (per("bwd_dq"), 6.0 * pair_flops),
-            "dkv": (per("bwd_dkv"), 8.0 * pair_flops)}
+            "dk": (per("bwd_dk"), 6.0 * pair_flops), "dv": (per("bwd_dv"), 4.0 * pair_flops)}
     for k, (ms, fl) in kern.items():
         log(f"{k}: {ms:.2f} ms per step, {fl / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
     log(f"merge {per('merge'):.3f} ms, copies {per('layout'):.3f} ms, row statistics {per('bwd_pre'):.3f} ms; "
@@ -487,7 +487,7 @@ def run_block_causal(args):
     dom = max(kern, key=lambda k: kern[k][0])
     dom_ms, dom_flops = kern[dom]
     launches = {"attention": prof["attn_launches"], "dq": prof["bwd_dq_launches"],
-                "dkv": prof["bwd_dkv_launches"]}[dom] / args.steps
+                "dk": prof["bwd_dk_launches"], "dv": prof["bwd_dv_launches"]}[dom] / args.steps
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     if args.calibration_copy:
         calibration_copy()
@@ -495,7 +495,7 @@ def run_block_causal(args):
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_block_causal(T, nh, d, n_latents, H, 1)
     src = "ff_kernels.hip" if dom == "attention" else "ff_bc_kernels.hip"
-    tag = {"attention": "attn", "dq": "bc_dq", "dkv": "bc_dkv"}[dom]
+    tag = {"attention": "attn", "dq": "bc_dq", "dk": "bc_dk", "dv": "bc_dv"}[dom]
     res = {
         "metric": "block-causal training attention TFLOP/s (forward + backward, % bf16 MFMA peak)",
         "value": round(tflops, 2),

@@ -4,14 +4,14 @@
 //  bc_dq<D>    dQ, query-major: item = (chunk, head, 256 queries); over the
 //              chunk's key tiles S^T = K Q^T, dP^T = V dO^T,
 //              dS^T = P^T * (dP^T - rowsum), dQ^T += K^T dS^T
-//  bc_dkv<D>   dK and dV, key-major: item = (source, head, 128 keys); over
+//  bc_dkv<D,.> dK or dV, key-major: item = (source, head, 256 keys); over
 //              the query tiles of every chunk that reads the source
-//              S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS
+//              S = Q K^T, then dV^T += dO^T P, or dP = dO V^T and dK^T += Q^T dS
 //  *_f32       plain fp32 paths (one lane per row and head)
 //
-// The two MFMA kernels split the work so that no gradient needs atomics:
-// each query row's dQ and each key row's dK/dV are owned by one workgroup,
-// at the price of computing S and dP twice.
+// The MFMA kernels split the work so that no gradient needs atomics: each
+// query row's dQ and each key row's dK and dV are owned by one workgroup, at
+// the price of computing S three times and dP twice.
 //
 // Page cited: [S] "In-Flight KV Cache with Clean Anchors for Faster
 // Autoregressive Video Diffusion", Korean summary page, section "how it
@@ -27,8 +27,8 @@ namespace ff {
 namespace {
 
 constexpr int kDqWaves = 8;              // two per SIMD, 32 queries each
-constexpr int kDkvWaves = 4;             // one per SIMD, 32 keys each (K, V, dK, dV live in registers)
-constexpr int kDkvKeys = kDkvWaves * 32;
+constexpr int kKeyWaves = 8;             // two per SIMD, 32 keys each
+constexpr int kKeyBlock = kKeyWaves * 32;
 
 // This wave's share of the copies of one rows tile (rows o .. o+63 of a
 // [n][D] block) into LDS; rows at or past n read as zeros.
@@ -256,34 +256,36 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bc_dq_kernel(const BcLaunch 
 }
 
 // --------------------------------------------------------------------------
-// dK, dV (bf16 MFMA).  Wave w owns keys 32w .. 32w+31 of the item's 128; per
-// 64-query tile and 32-query half (lane = key column, registers = queries):
+// dK or dV (bf16 MFMA), key-major.  Wave w owns keys 32w .. 32w+31 of the
+// item's 256; per 64-query tile and 32-query half (lane = key column,
+// registers = queries):
 //   S  = Q K^T            A = Q rows (LDS),   B = K (registers)
-//   dP = dO V^T           A = dO rows (LDS),  B = V (registers)
-//   P  = 2^(S*scale*log2e - lse*log2e),  dS = P * (dP - rowsum)
-//   dV^T += dO^T P        A = dO^T (LDS),     B = P (bf16)
-//   dK^T += Q^T dS        A = Q^T (LDS),      B = dS (bf16)
-// The per-query statistics of a tile (512 bytes) are copied with it.
+//   P  = 2^(S*scale*log2e - lse*log2e)
+// dV:  dV^T += dO^T P     A = dO^T (LDS),     B = P (bf16)
+// dK:  dP = dO V^T        A = dO rows (LDS),  B = V (registers)
+//      dS = P * (dP - rowsum),  dK^T += Q^T dS   A = Q^T (LDS), B = dS (bf16)
+// dK and dV run as two kernels: one kernel holding K, V, dK and dV for its
+// keys needs more than the 256 registers of a wave that shares its SIMD, and
+// with a single wave per SIMD nothing hides the operand reads.  The per-query
+// statistics of a tile (512 bytes) are copied with it.
 // --------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(kDkvWaves * 64, 1) void bc_dkv_kernel(const BcLaunch b) {
-  constexpr int NW = kDkvWaves;
+template <int D, bool kDK>
+__global__ __launch_bounds__(kKeyWaves * 64, 1) void bc_dkv_kernel(const BcLaunch b) {
+  constexpr int NW = kKeyWaves;
   constexpr int KS = D / 16, DB = D / 32;
   using Cfg = TileCfg<D, NW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t qr0[Cfg::kKBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t qr0[Cfg::kKBytes];   // Q rows
   __shared__ __attribute__((aligned(1024))) uint8_t qr1[Cfg::kKBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t gr0[Cfg::kKBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t gr1[Cfg::kKBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t qt0[Cfg::kVBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t qt1[Cfg::kVBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t gt0[Cfg::kVBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t gt1[Cfg::kVBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t gr0[kDK ? Cfg::kKBytes : 1024];   // dO rows (dK)
+  __shared__ __attribute__((aligned(1024))) uint8_t gr1[kDK ? Cfg::kKBytes : 1024];
+  __shared__ __attribute__((aligned(1024))) uint8_t tt0[Cfg::kVBytes];   // Q^T (dK) or dO^T (dV)
+  __shared__ __attribute__((aligned(1024))) uint8_t tt1[Cfg::kVBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t st0[1024];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[1024];
 
   // Items: chunk sources first (they have the most readers), then anchors.
-  const int nkb_c = (b.L + kDkvKeys - 1) / kDkvKeys;
-  const int nkb_a = (b.T + kDkvKeys - 1) / kDkvKeys;
+  const int nkb_c = (b.L + kKeyBlock - 1) / kKeyBlock;
+  const int nkb_a = (b.T + kKeyBlock - 1) / kKeyBlock;
   int item = xcd_remap(blockIdx.x, gridDim.x);     // key blocks of one (source, head) share an XCD
   const bool is_chunk = item < b.n_chunk * b.nh * nkb_c;
   int src, n, h, kb;
@@ -300,33 +302,28 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bc_dkv_kernel(const BcLaunc
     n = b.T;
   }
   const BcReaders rd = b.readers[is_chunk ? kBcMaxAnchors + src : src];
-  const void* Kin = is_chunk ? b.K : b.Ka;
-  const void* Vin = is_chunk ? b.V : b.Va;
   const int64_t row0 = int64_t(src) * n;          // first token row of the source
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, hl = lane >> 5;
-  const int key = kb * kDkvKeys + w * 32 + l32;
+  const int key = kb * kKeyBlock + w * 32 + l32;
   const bool kok = key < n;
 
   bf16x8 kreg[1][KS], vreg[1][KS];
-  load_b_operand<D>(Kin, row0 + key, b.nh, h, kok, hl, kreg);
-  load_b_operand<D>(Vin, row0 + key, b.nh, h, kok, hl, vreg);
+  load_b_operand<D>(is_chunk ? b.K : b.Ka, row0 + key, b.nh, h, kok, hl, kreg);
+  if (kDK) load_b_operand<D>(is_chunk ? b.V : b.Va, row0 + key, b.nh, h, kok, hl, vreg);
   const float c = b.scale * kLog2e;
 
   LaneConst<D, NW> lc;
   lane_const<D, NW>(lc, w, lane);
   uint32_t toff[Cfg::kVBlocks];
   tr_offsets<D, NW>(toff, b.L, w, lane);
-  f32x16 dk[DB], dv[DB];
+  f32x16 acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.f;
-      dv[db][r] = 0.f;
-    }
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
   const int nqt = (b.L + kBlockN - 1) / kBlockN;
   const int ntiles = rd.n * nqt;
@@ -337,9 +334,8 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bc_dkv_kernel(const BcLaunc
     const __bf16* gg = reinterpret_cast<const __bf16*>(b.gg_chunk + int64_t(i) * b.blk_chunk);
     const int64_t rows = int64_t(h) * b.L * D, tr = int64_t(b.nh) * b.L * D + int64_t(h) * D * b.L;
     copy_rows<D, NW>(qq + rows, b.L, o, lc, p ? qr1 : qr0, w);
-    copy_rows<D, NW>(gg + rows, b.L, o, lc, p ? gr1 : gr0, w);
-    copy_tr<D, NW>(qq + tr, b.L, o, toff, p ? qt1 : qt0, w);
-    copy_tr<D, NW>(gg + tr, b.L, o, toff, p ? gt1 : gt0, w);
+    if (kDK) copy_rows<D, NW>(gg + rows, b.L, o, lc, p ? gr1 : gr0, w);
+    copy_tr<D, NW>((kDK ? qq : gg) + tr, b.L, o, toff, p ? tt1 : tt0, w);
     if (w == 0) {
       // 64 queries x {-lse*log2e, rowsum}: the first 512 bytes of a 1 KB copy.
       const float* sp = b.stats + 2 * ((int64_t(i) * b.nh + h) * b.L + o);
@@ -352,21 +348,20 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bc_dkv_kernel(const BcLaunc
   for (int t = 0; t < ntiles; ++t) {
     const int p = t & 1;
     wait_dma();
-    __syncthreads();
+    __syncthreads();                      // tile t landed everywhere; tile t-1's buffers are free
     const int valid_next = t + 1 < ntiles ? issue(t + 1, p ^ 1) : 0;
     const uint8_t* qb = p ? qr1 : qr0;
     const uint8_t* gb = p ? gr1 : gr0;
-    const uint8_t* qtb = p ? qt1 : qt0;
-    const uint8_t* gtb = p ? gt1 : gt0;
+    const uint8_t* tb = p ? tt1 : tt0;
     const float* stb = reinterpret_cast<const float*>(p ? st1 : st0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x16 sc[1], dp[1];
       qk_half<D, NW, 1>(qb, half, lc, kreg, sc);
-      qk_half<D, NW, 1>(gb, half, lc, vreg, dp);
+      if (kDK) qk_half<D, NW, 1>(gb, half, lc, vreg, dp);
       const int lim = valid - 32 * half;
       if (lim < 32) mask_half(sc[0], lim, hl);
-      bf16x8 pb[2], dsb[2];
+      bf16x8 ob[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         // registers 8j .. 8j+7 hold queries 32*half + 16j + 8*hl + 0..7
@@ -380,18 +375,16 @@ __global__ __launch_bounds__(kDkvWaves * 64, 1) void bc_dkv_kernel(const BcLaunc
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float pv = __builtin_amdgcn_exp2f(fmaf(sc[0][8 * j + e], c, stv[2 * e]));
-          pb[j][e] = (__bf16)pv;
-          dsb[j][e] = (__bf16)(pv * (dp[0][8 * j + e] - stv[2 * e + 1]));
+          ob[j][e] = kDK ? (__bf16)(pv * (dp[0][8 * j + e] - stv[2 * e + 1])) : (__bf16)pv;
         }
       }
-      tr_mfma_half<D, NW>(gtb, half, lc, pb, dv);
-      tr_mfma_half<D, NW>(qtb, half, lc, dsb, dk);
+      tr_mfma_half<D, NW>(tb, half, lc, ob, acc);
     }
     valid = valid_next;
   }
   if (kok) {
-    store_rows<D>(is_chunk ? b.dK : b.dKa, row0 + key, b.nh, h, hl, b.scale, dk);
-    store_rows<D>(is_chunk ? b.dV : b.dVa, row0 + key, b.nh, h, hl, 1.0f, dv);
+    if (kDK) store_rows<D>(is_chunk ? b.dK : b.dKa, row0 + key, b.nh, h, hl, b.scale, acc);
+    else store_rows<D>(is_chunk ? b.dV : b.dVa, row0 + key, b.nh, h, hl, 1.0f, acc);
   }
 }
 
@@ -505,7 +498,7 @@ void launch_backward(const BcLaunch& b, hipStream_t s, Profiler* prof) {
       hipLaunchKernelGGL(bc_dq_f32_kernel<D>, dim3(unsigned((rows + 63) / 64)), dim3(64), 0, s, b);
     }
     {
-      Timed tm(prof, kBwdDkv, s);
+      Timed tm(prof, kBwdDk, s);
       const int64_t keys = (int64_t(b.n_chunk) * b.L + int64_t(b.n_anchor) * b.T) * b.nh;
       hipLaunchKernelGGL(bc_dkv_f32_kernel<D>, dim3(unsigned((keys + 63) / 64)), dim3(64), 0, s, b);
     }
@@ -516,11 +509,15 @@ void launch_backward(const BcLaunch& b, hipStream_t s, Profiler* prof) {
     const int items = b.n_chunk * b.nh * ((b.L + kBlockM - 1) / kBlockM);
     hipLaunchKernelGGL(bc_dq_kernel<D>, dim3(unsigned(items)), dim3(kDqWaves * 64), 0, s, b);
   }
+  const int items = (b.n_chunk * ((b.L + kKeyBlock - 1) / kKeyBlock) +
+                     b.n_anchor * ((b.T + kKeyBlock - 1) / kKeyBlock)) * b.nh;
   {
-    Timed tm(prof, kBwdDkv, s);
-    const int items = (b.n_chunk * ((b.L + kDkvKeys - 1) / kDkvKeys) +
-                       b.n_anchor * ((b.T + kDkvKeys - 1) / kDkvKeys)) * b.nh;
-    hipLaunchKernelGGL(bc_dkv_kernel<D>, dim3(unsigned(items)), dim3(kDkvWaves * 64), 0, s, b);
+    Timed tm(prof, kBwdDk, s);
+    hipLaunchKernelGGL((bc_dkv_kernel<D, true>), dim3(unsigned(items)), dim3(kKeyWaves * 64), 0, s, b);
+  }
+  {
+    Timed tm(prof, kBwdDv, s);
+    hipLaunchKernelGGL((bc_dkv_kernel<D, false>), dim3(unsigned(items)), dim3(kKeyWaves * 64), 0, s, b);
   }
 }
 

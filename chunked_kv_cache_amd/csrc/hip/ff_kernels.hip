@@ -793,7 +793,8 @@ int dev_profiler_read(Profiler* p, ff_kernel_times* out) {
   out->layout_launches = p->count[kLayout]; out->layout_ms = p->ms[kLayout];
   out->bwd_pre_launches = p->count[kBwdPre]; out->bwd_pre_ms = p->ms[kBwdPre];
   out->bwd_dq_launches = p->count[kBwdDq];  out->bwd_dq_ms = p->ms[kBwdDq];
-  out->bwd_dkv_launches = p->count[kBwdDkv]; out->bwd_dkv_ms = p->ms[kBwdDkv];
+  out->bwd_dk_launches = p->count[kBwdDk];  out->bwd_dk_ms = p->ms[kBwdDk];
+  out->bwd_dv_launches = p->count[kBwdDv];  out->bwd_dv_ms = p->ms[kBwdDv];
   return rc;
 }
 

@@ -12,7 +12,7 @@
 namespace ff {
 
 // Kernel families timed separately (the fields of ff_kernel_times).
-enum { kAttn = 0, kMerge, kPublish, kAnchor, kLayout, kBwdPre, kBwdDq, kBwdDkv, kKinds };
+enum { kAttn = 0, kMerge, kPublish, kAnchor, kLayout, kBwdPre, kBwdDq, kBwdDk, kBwdDv, kKinds };
 
 struct Profiler {
   struct Rec { int kind; hipEvent_t a, b; };

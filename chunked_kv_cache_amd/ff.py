@@ -47,7 +47,8 @@ class ff_kernel_times(ctypes.Structure):
                 ("layout_launches", ctypes.c_int64), ("layout_ms", ctypes.c_double),
                 ("bwd_pre_launches", ctypes.c_int64), ("bwd_pre_ms", ctypes.c_double),
                 ("bwd_dq_launches", ctypes.c_int64), ("bwd_dq_ms", ctypes.c_double),
-                ("bwd_dkv_launches", ctypes.c_int64), ("bwd_dkv_ms", ctypes.c_double)]
+                ("bwd_dk_launches", ctypes.c_int64), ("bwd_dk_ms", ctypes.c_double),
+                ("bwd_dv_launches", ctypes.c_int64), ("bwd_dv_ms", ctypes.c_double)]
 
 
 class FFError(RuntimeError):

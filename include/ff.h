@@ -109,7 +109,8 @@ typedef struct {
   int64_t layout_launches;  double layout_ms;    /* block-causal operand copies */
   int64_t bwd_pre_launches; double bwd_pre_ms;   /* rowsum(dO*O), -lse*log2(e)  */
   int64_t bwd_dq_launches;  double bwd_dq_ms;    /* dQ (query-major)           */
-  int64_t bwd_dkv_launches; double bwd_dkv_ms;   /* dK, dV (key-major)         */
+  int64_t bwd_dk_launches;  double bwd_dk_ms;    /* dK (key-major; fp32: dK+dV) */
+  int64_t bwd_dv_launches;  double bwd_dv_ms;    /* dV (key-major)             */
 } ff_kernel_times;
 
 /* Bytes of device workspace for a context with n_stages banks of history H.
