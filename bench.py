@@ -59,6 +59,8 @@ WORKLOADS = {
     # block-causal training form: forward + backward of one stage over a whole clip
     "bc480": (1560, 12, 0, 81, 1, "480p block-causal training pass: forward + backward of one stage over the "
                                   "81-latent clip (27 chunks of 4680 queries, 9 anchors), 12 heads x 128"),
+    "bc720": (3600, 40, 0, 81, 1, "720p block-causal training pass: forward + backward of one stage over the "
+                                  "81-latent clip (27 chunks of 10800 queries, 9 anchors), 40 heads x 128"),
 }
 
 
@@ -508,7 +510,8 @@ def run_block_causal(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO and anchors drawn on the device, 480p clip shapes)",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V/dO and anchors drawn on the device, clip shapes of the "
+                "workload)",
         "config": {"workload": desc, "chunks": nc, "anchors": na, "queries_per_chunk": L, "heads": nh,
                    "head_dim": d, "history": H, "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),

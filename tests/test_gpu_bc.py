@@ -212,3 +212,25 @@ def test_bc_480p_sampled():
     r = check(case, mine, O, LSE, grads, rows=rows,
               sources={"dK": key_rows, "dV": key_rows, "dKa": anc_rows, "dVa": anc_rows})
     print("bc 480p head 5:", r)
+
+
+def test_bc_720p_last_chunk():
+    """720p clip (T=3600, 40 heads, d=128, 81 latents: 10800-query chunks, 72000 keys) run whole
+    on the GPU; one head checked on chunk 26, which alone completes the gradients of its own keys."""
+    case = BcCase(T=3600, nh=40, d=128)
+    cfg = case.cfg
+    host = case.inputs()
+    h = 17
+    mine = run_gpu(case, host, head=h)
+    one = [syn.as_f64(x[:, h:h + 1, :], case.dtype) for x in host]
+    del host
+    cfg1 = orc.FFConfig(tokens_per_latent=case.T, n_heads=1, head_dim=case.d)
+    chunks = [26]
+    O, LSE = orc.bc_forward(cfg1, *one[:5], chunks=chunks)
+    grads = orc.bc_backward(cfg1, *one, chunks=chunks)
+    anchors, srcs = orc.bc_complete_sources(cfg, chunks)
+    assert srcs == [26] and anchors == []
+    L = cfg.chunk_tokens
+    rows = np.arange(26 * L, 27 * L)
+    r = check(case, mine, O, LSE, grads, rows=rows, sources={"dK": rows, "dV": rows, "dKa": [], "dVa": []})
+    print("bc 720p head 17 chunk 26:", r)
