@@ -164,6 +164,16 @@ def test_bc_bf16_head_dim_64_peaked():
     print("bc bf16 d=64 peaked:", r)
 
 
+@pytest.mark.parametrize("case", [
+    BcCase(T=8, nh=1, d=128, n_latents=24, H=1, dtype="f32"),          # fp32 at d=128, one history chunk
+    BcCase(T=64, nh=2, d=128, n_latents=30, H=1, rule=orc.GAMMA_CENTER_LR),   # whole 64-query tiles
+    BcCase(T=8, nh=4, d=64, n_latents=12, H=5),                        # smallest tiles, bank never full
+], ids=["f32_d128_H1", "bf16_center_lr_H1", "bf16_T8"])
+def test_bc_small_edge_cases(case):
+    r = full_case(case)
+    print(f"bc edge {case.dtype} T={case.T} d={case.d} H={case.H}:", r)
+
+
 def test_bc_forward_equals_inference_calls():
     """Chunk i's forward rows equal ff_render_attend(i, 0) on the same bytes, bit for bit."""
     import torch
