@@ -122,6 +122,7 @@ template <int D>
 struct WaveState {
   f32x16 o[D / 32];          // O^T accumulators, one per 32-row block of d
   float m, l;                // running max (base 2) and per-lane partial sum
+  float thr;                 // (m + threshold) / c: raw-score level that moves the max
 };
 
 
@@ -141,10 +142,9 @@ __device__ __forceinline__ float rowmax_half(const f32x16& s) {
 // Raise the running max when a half's max exceeds it by more than the
 // threshold, rescaling O and the partial sum; run before that half's exps.
 template <int D>
-__device__ __forceinline__ void rescale(float mx, float c, WaveState<D>& st) {
-  const float mx2 = mx * c;
-  if (__builtin_expect(__ballot(mx2 > st.m + kRescaleTau) != 0, 0)) {
-    const float m_new = fmaxf(st.m, mx2);
+__device__ __forceinline__ void rescale(float mx, float c, float inv_c, WaveState<D>& st) {
+  if (__builtin_expect(__ballot(mx > st.thr) != 0, 0)) {
+    const float m_new = fmaxf(st.m, mx * c);
     const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
     st.l *= alpha;
 #pragma unroll
@@ -152,24 +152,31 @@ __device__ __forceinline__ void rescale(float mx, float c, WaveState<D>& st) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
     st.m = m_new;
+    st.thr = (m_new + kRescaleTau) * inv_c;
   }
 }
 
-// P = 2^(s*c - m) as bf16 B operands, and the partial row sum (branch-free).
+// P = 2^(s*c - m) as bf16 B operands, and the partial row sum (branch-free;
+// two chains of 8, each starting from its first term).
 template <int D>
 __device__ __forceinline__ void softmax_p(const f32x16& s, float c, WaveState<D>& st, bf16x8 (&pb)[2]) {
   const float nm = -st.m;
-  float lsum = 0.f;
+  float lsum[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float pv = __builtin_amdgcn_exp2f(fmaf(s[8 * j + e], c, nm));
-      lsum += pv;
+      lsum[j] = e ? lsum[j] + pv : pv;
       pb[j][e] = (__bf16)pv;
     }
-  st.l += lsum;
+  st.l += lsum[0] + lsum[1];
 }
+
+// Pin a value at this program point: the row-sum additions are then issued
+// in the same basic block as the MFMAs they can overlap, instead of being
+// sunk past the masking branch that follows.
+__device__ __forceinline__ void materialize(float& x) { asm volatile("" : "+v"(x)); }
 
 // O^T += V^T P^T for one 32-key half of the V^T tile vbuf; each operand read
 // feeds R MFMAs.
@@ -230,6 +237,7 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
   }
 
   const float c = a.scale * kLog2e;
+  const float inv_c = 1.0f / c;
   LaneConst<D, NW> lc;
   lane_const<D, NW>(lc, w, lane);
 
@@ -241,6 +249,7 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[b].o[db][r] = 0.f;
     st[b].m = -INFINITY;
+    st[b].thr = -INFINITY;
     st[b].l = 0.f;
   }
 
@@ -270,7 +279,7 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
       }
     }
 #pragma unroll
-    for (int b = 0; b < R; ++b) rescale<D>(mx[b], c, st[b]);
+    for (int b = 0; b < R; ++b) rescale<D>(mx[b], c, inv_c, st[b]);
   };
   auto softmax = [&](const f32x16 (&s)[R], bf16x8 (&pb)[R][2]) {
 #pragma unroll
@@ -301,6 +310,8 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     qk_half<D, NW, R>(lb.k[i], 1, lc, qreg, sb);
     softmax(sa, pb);
     pv_half<D, NW, R>(lb.v[i], 0, lc, pb, st);
+#pragma unroll
+    for (int b = 0; b < R; ++b) materialize(st[b].l);
     finish_scores(sb, valid[i] - 32);
     // half 1: S^T(tile t+1, half 0) and softmax(half 1); then PV(half 1).
     // On the last tile the S^T of buffer i+1 is computed on stale data and dropped.
@@ -314,6 +325,8 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     qk_half<D, NW, R>(lb.k[i1], 0, lc, qreg, sa);
     softmax(sb, pb);
     pv_half<D, NW, R>(lb.v[i], 1, lc, pb, st);
+#pragma unroll
+    for (int b = 0; b < R; ++b) materialize(st[b].l);
     if (more) finish_scores(sa, valid[i1]);
   };
 
