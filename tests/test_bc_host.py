@@ -197,3 +197,28 @@ def test_argument_checks():
         assert ff.ff_bc_workspace_bytes(ok, 5, L=hb.L) > 0
     finally:
         hb.close()
+
+
+def test_product_library_validates_block_causal_calls_before_device_work():
+    """libff.so checks the block-causal calls before touching the GPU, so these run on a CPU host."""
+    L = ff.load(ff.LIB_PATH)
+    shape = ff.make_shape(n_heads=2, head_dim=128, tokens_per_latent=16)
+    need = ff.ff_bc_workspace_bytes(shape, 5, L=L)
+    assert need > 0
+    raw, addr = _aligned_buffer(need)
+    bc = ff.ff_bc_create(shape, 5, addr, need, L=L)
+    try:
+        with pytest.raises(ff.FFError) as e:
+            ff.ff_bc_forward(bc, None, FAKE, FAKE, FAKE, FAKE, FAKE, L=L)
+        assert e.value.status == ff.FF_E_INVAL
+        with pytest.raises(ff.FFError) as e:        # lse is required by the backward
+            ff.ff_bc_backward(bc, *[FAKE] * 6, None, *[FAKE] * 6, L=L)
+        assert e.value.status == ff.FF_E_INVAL
+        assert ff.ff_bc_key_plan(bc, 26, L=L).key_tokens == 16 * 20
+    finally:
+        ff.ff_bc_destroy(bc, L=L)
+    bad = ff.make_shape(n_heads=2, head_dim=96, tokens_per_latent=16)
+    assert ff.ff_bc_workspace_bytes(bad, 5, L=L) == 0
+    with pytest.raises(ff.FFError) as e:
+        ff.ff_bc_create(bad, 5, addr, need, L=L)
+    assert e.value.status == ff.FF_E_INVAL
