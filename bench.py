@@ -320,6 +320,26 @@ def run_rollout(args):
     log(f"rollout: {n_calls} calls in {len(sched)} diagonals, median {dt * 1e3:.1f} ms "
         f"(min {min(times) * 1e3:.1f}), {flops / 1e12:.1f} TFLOP, {tflops:.1f} TFLOP/s, "
         f"{n_calls / dt:.0f} chunk-steps/s")
+    # One more rollout with per-kernel HIP events (outside the timed ones): the
+    # Tail_H publishes of a grouped launch move every pair's K/V at once.
+    orig_create = ff.ff_stage_bank_create
+
+    def create_profiled(*a, **k):
+        ctx = orig_create(*a, **k)
+        ff.ff_profile_enable(ctx, True)
+        return ctx
+    ff.ff_stage_bank_create = create_profiled
+    try:
+        rollout()
+    finally:
+        ff.ff_stage_bank_create = orig_create
+    prof = ff.ff_profile_read(banks.ctx)
+    pub_bytes = n_calls * 2 * 2 * Lq * nh * d * 2                # K and V of every call, read + write
+    pub_gbps = pub_bytes / (prof["publish_ms"] * 1e-3) / 1e9
+    attn_tflops = flops / (prof["attn_ms"] * 1e-3) / 1e12
+    log(f"kernels: attention {prof['attn_ms']:.1f} ms ({attn_tflops:.1f} TFLOP/s) in {prof['attn_launches']} "
+        f"launches; publish {prof['publish_ms']:.2f} ms in {prof['publish_launches']} launches "
+        f"({pub_gbps:.0f} GB/s, {100 * pub_gbps / PEAK_HBM_GBPS:.1f}% of HBM)")
     res = {
         "metric": "renderer rollout TFLOP/s (% bf16 MFMA peak) + chunk-steps/s",
         "value": round(tflops, 2),
@@ -338,6 +358,10 @@ def run_rollout(args):
                    "rollout_tflop": round(flops / 1e12, 2), "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "chunk_steps_per_s": round(n_calls / dt, 1),
+        "attention_kernel_tflops": round(attn_tflops, 1),
+        "publish_launches": prof["publish_launches"],
+        "publish_gbps": round(pub_gbps, 1),
+        "publish_pct_hbm": round(100 * pub_gbps / PEAK_HBM_GBPS, 2),
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
