@@ -101,7 +101,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the stage-sharded multi-GPU path is a design, not part of this build)", file=sys.stderr)
+              "(the library runs one GPU's share; the stage-sharded multi-GPU layout is a design only)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
