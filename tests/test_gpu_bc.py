@@ -174,6 +174,34 @@ def test_bc_small_edge_cases(case):
     print(f"bc edge {case.dtype} T={case.T} d={case.d} H={case.H}:", r)
 
 
+def test_bc_context_reused_across_calls():
+    """Two forward + backward passes with different inputs on one context: the
+    workspace is scratch, so the second result depends on its own inputs only."""
+    import torch
+    cases = [BcCase(T=64, nh=2, d=128, n_latents=24, H=2, seed=s) for s in (3, 4)]
+    bc = ff.BlockCausal(cases[0].shape(), cases[0].H)
+    try:
+        bc.workspace.view(torch.int16).fill_(0x7FC0)
+        for case in cases:
+            host = case.inputs()
+            Ka, Va, Q, K, V, dO = (to_device(x, case.dtype) for x in host)
+            nc, L = orc.n_chunks(case.cfg), case.cfg.chunk_tokens
+            O = _nan_like(Q)
+            lse = torch.full((nc, case.nh, L), float("nan"), dtype=torch.float32, device="cuda")
+            ff.ff_bc_forward(bc.ctx, Ka, Va, Q, K, V, O, lse)
+            grads = [_nan_like(x) for x in (Q, K, V, Ka, Va)]
+            ff.ff_bc_backward(bc.ctx, Ka, Va, Q, K, V, O, lse, dO, *grads)
+            torch.cuda.synchronize()
+            f64 = [syn.as_f64(x, case.dtype) for x in host]
+            O_ref, LSE_ref = orc.bc_forward(case.cfg, *f64[:5])
+            refs = orc.bc_backward(case.cfg, *f64)
+            got = dict(O=from_device_f64(O), lse=from_device_f64(lse),
+                       **{n: from_device_f64(g) for n, g in zip(("dQ", "dK", "dV", "dKa", "dVa"), grads)})
+            check(case, got, O_ref, LSE_ref, refs)
+    finally:
+        bc.close()
+
+
 def test_bc_forward_equals_inference_calls():
     """Chunk i's forward rows equal ff_render_attend(i, 0) on the same bytes, bit for bit."""
     import torch
