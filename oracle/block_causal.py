@@ -13,7 +13,7 @@ that in self-rollout distillation the renderer runs as one block-causal
 forward over the clip instead of per-chunk cache updates, so that gradients
 reach earlier chunks from later ones and the planner from the renderer.
 
-Readings taken (also listed in the design doc):
+Readings taken where the pages leave a step open:
   R13 The block-causal forward at one stage gives chunk i's queries exactly
       the keys of the inference call (i, k) once its bank is in steady state:
       the anchors of Gamma(i), chunks max(0, i-H) .. i-1 of the same stage

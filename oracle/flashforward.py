@@ -18,7 +18,7 @@ Pages cited (title, then the part of the page):
   [C] "In-Flight KV Cache 与 Clean Anchors：更快的自回归视频扩散" -- Chinese notes,
       section 方法 (method).
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   R1  Gamma(i) is never written out.  Default "bracket": every anchor whose
       position lies in [D*floor(first/D), D*ceil(last/D)] for the chunk's first
       and last latent positions (two-sided for every latent of the chunk).
