@@ -87,6 +87,9 @@ CONFIGS = [
     dict(tokens_per_latent=16, n_heads=2, head_dim=64, n_latents=36, w_ctx=11),
     dict(tokens_per_latent=16, n_heads=2, head_dim=128, gamma_rule=orc.GAMMA_CENTER_LR),
     dict(tokens_per_latent=8, n_heads=1, head_dim=64, n_latents=261),
+    dict(tokens_per_latent=8, n_heads=1, head_dim=64, n_latents=288, history=8),        # 96 chunks, H max
+    dict(tokens_per_latent=8, n_heads=1, head_dim=64, n_latents=60, history=1, w_ctx=5),
+    dict(tokens_per_latent=8, n_heads=1, head_dim=64, n_latents=45, anchor_stride=7),  # stride not 10
 ]
 
 
