@@ -42,15 +42,17 @@ class BcCase:
     dtype: str = "bf16"
     seed: int = 0
     q_scale: float = 1.0
+    stride: int = 10
 
     @property
     def cfg(self):
         return orc.FFConfig(tokens_per_latent=self.T, n_heads=self.nh, head_dim=self.d, n_latents=self.n_latents,
-                            history=self.H, w_ctx=self.w_ctx, gamma_rule=self.rule)
+                            history=self.H, w_ctx=self.w_ctx, gamma_rule=self.rule, anchor_stride=self.stride)
 
     def shape(self):
         return ff.make_shape(n_heads=self.nh, head_dim=self.d, tokens_per_latent=self.T, n_latents=self.n_latents,
-                             w_ctx=self.w_ctx, dtype=ff.FF_BF16 if self.dtype == "bf16" else ff.FF_F32,
+                             anchor_stride=self.stride, w_ctx=self.w_ctx,
+                             dtype=ff.FF_BF16 if self.dtype == "bf16" else ff.FF_F32,
                              gamma_rule=ff.FF_GAMMA_BRACKET if self.rule == orc.GAMMA_BRACKET
                              else ff.FF_GAMMA_CENTER_LR)
 
@@ -168,7 +170,8 @@ def test_bc_bf16_head_dim_64_peaked():
     BcCase(T=8, nh=1, d=128, n_latents=24, H=1, dtype="f32"),          # fp32 at d=128, one history chunk
     BcCase(T=64, nh=2, d=128, n_latents=30, H=1, rule=orc.GAMMA_CENTER_LR),   # whole 64-query tiles
     BcCase(T=8, nh=4, d=64, n_latents=12, H=5),                        # smallest tiles, bank never full
-], ids=["f32_d128_H1", "bf16_center_lr_H1", "bf16_T8"])
+    BcCase(T=24, nh=2, d=128, n_latents=45, H=8, w_ctx=30, stride=7),  # H = 8, anchor stride 7
+], ids=["f32_d128_H1", "bf16_center_lr_H1", "bf16_T8", "bf16_H8_stride7"])
 def test_bc_small_edge_cases(case):
     r = full_case(case)
     print(f"bc edge {case.dtype} T={case.T} d={case.d} H={case.H}:", r)
