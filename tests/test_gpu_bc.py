@@ -171,7 +171,9 @@ def test_bc_bf16_head_dim_64_peaked():
     BcCase(T=64, nh=2, d=128, n_latents=30, H=1, rule=orc.GAMMA_CENTER_LR),   # whole 64-query tiles
     BcCase(T=8, nh=4, d=64, n_latents=12, H=5),                        # smallest tiles, bank never full
     BcCase(T=24, nh=2, d=128, n_latents=45, H=8, w_ctx=30, stride=7),  # H = 8, anchor stride 7
-], ids=["f32_d128_H1", "bf16_center_lr_H1", "bf16_T8", "bf16_H8_stride7"])
+    BcCase(T=16, nh=2, d=128, n_latents=3),                            # one chunk, one anchor
+    BcCase(T=16, nh=2, d=128, n_latents=6),                            # two chunks, one anchor
+], ids=["f32_d128_H1", "bf16_center_lr_H1", "bf16_T8", "bf16_H8_stride7", "bf16_1chunk", "bf16_2chunks"])
 def test_bc_small_edge_cases(case):
     r = full_case(case)
     print(f"bc edge {case.dtype} T={case.T} d={case.d} H={case.H}:", r)

@@ -51,6 +51,14 @@ def test_bf16_rollout_multi_tile_ragged(rule):
           f"lse={st.max_lse:.2e} control>={st.min_control_ratio:.1f}x")
 
 
+@pytest.mark.parametrize("n_latents", [3, 9])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_degenerate_short_clips(n_latents, dtype):
+    """The shortest clips: one chunk and one anchor (3 latents), three chunks sharing one anchor (9)."""
+    st = _rollout(Case(T=16, nh=2, d=128 if dtype == "bf16" else 64, n_latents=n_latents, S=2, dtype=dtype))
+    assert st.calls == 2 * (n_latents // 3) and st.bank_checks == st.calls
+
+
 def test_bf16_head_dim_64_and_peaked_softmax():
     st = _rollout(Case(T=40, nh=3, d=64, S=2, q_scale=8.0))
     assert st.calls == 54
