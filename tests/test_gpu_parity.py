@@ -152,6 +152,16 @@ def test_planner_rollout_tiny_fp32():
     print(f"planner fp32: max|dO|={st.max_abs:.2e} relF={st.max_rel_fro:.2e} lse={st.max_lse:.2e}")
 
 
+@pytest.mark.parametrize("n_latents", [3, 42])
+def test_planner_short_blocks(n_latents):
+    """A lone one-anchor block (3 latents), and a last block shorter than B_P
+    (42 latents: anchors 0, 10, .., 40 in blocks of 3 and 2)."""
+    case = Case(T=16, nh=2, d=128, n_latents=n_latents, S=2)
+    n_blocks = len(orc.planner_blocks(case.cfg))
+    st = _planner_rollout(case, render_diags=3)
+    assert st.calls == 3 * n_blocks + sum(len(d) for d in orc.schedule(case.cfg)[:3])
+
+
 @pytest.mark.parametrize("h_p", [6, 2])
 def test_planner_rollout_bf16_multi_tile(h_p):
     """bf16, T=120 (360 queries: 2 query tiles, ragged), 261 latents: block 8
