@@ -262,7 +262,6 @@ def run_rollout(args):
     (values do not change the work; the pool keeps setup short)."""
     import torch
 
-    import oracle as orc
     from chunked_kv_cache_amd import ff
 
     T, nh, _, n_latents, S, desc = WORKLOADS[args.workload]
@@ -275,11 +274,12 @@ def run_rollout(args):
     pool = [(randn(Lq), randn(Lq), randn(Lq)) for _ in range(8)]
     shape = ff.make_shape(n_heads=nh, head_dim=d, tokens_per_latent=T, n_latents=n_latents)
     banks = ff.StageBanks(shape, S, H)
-    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=nh, head_dim=d, n_latents=n_latents, n_stages=S)
-    sched = orc.schedule(cfg)
+    # The library's own wavefront schedule and planner blocks.
+    counts = ff.ff_clip_layout(shape, S)
+    sched = [ff.ff_wavefront(shape, S, t) for t in range(counts["n_diagonals"])]
     n_calls = sum(len(x) for x in sched)
     outs = [torch.empty((Lq, nh, d), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
-    blocks = orc.planner_blocks(cfg)
+    blocks = [ff.ff_planner_block(shape, b) for b in range(counts["n_planner_blocks"])]
     anchor_kv = [(randn(len(b) * T), randn(len(b) * T)) for b in blocks]
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -460,15 +460,15 @@ def run_block_causal(args):
     over every chunk's key set, row statistics, dQ and dK/dV kernels)."""
     import torch
 
-    import oracle as orc
     from chunked_kv_cache_amd import ff
 
     T, nh, _, n_latents, _, desc = WORKLOADS[args.workload]
     d, H = 128, 5
     torch.cuda.set_device(0)
-    cfg = orc.FFConfig(tokens_per_latent=T, n_heads=nh, head_dim=d, n_latents=n_latents, history=H)
-    nc, na, L = orc.n_chunks(cfg), orc.n_anchors(cfg), cfg.chunk_tokens
-    bc = ff.BlockCausal(ff.make_shape(n_heads=nh, head_dim=d, tokens_per_latent=T, n_latents=n_latents), H)
+    shape = ff.make_shape(n_heads=nh, head_dim=d, tokens_per_latent=T, n_latents=n_latents)
+    counts = ff.ff_clip_layout(shape)
+    nc, na, L = counts["n_chunks"], counts["n_anchors"], shape.chunk_latents * T
+    bc = ff.BlockCausal(shape, H)
     t0 = time.time()
     # Seeded N(0,1) bf16 drawn on the device (the clip is 1.6 GB of inputs).
     gen = torch.Generator(device="cuda").manual_seed(0)

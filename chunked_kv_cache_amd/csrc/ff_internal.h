@@ -17,7 +17,8 @@ constexpr int kMaxSeg = 24;        // renderer: <= 3 anchors + 8 history chunks 
 constexpr int kMaxPairs = 8;       // renderer calls fused into one launch
 constexpr int kMaxHistory = 8;
 constexpr int kBlockM = 256;       // query rows per attention work item (8 waves x 32)
-constexpr int kCUs = 256;          // MI355X compute units (one work item each)
+constexpr int kMaxWg = 256;        // persistent attention workgroups at most (one per CU; the
+                                   // device's CU count is queried at context creation)
 constexpr int kBlockN = 64;        // keys per LDS tile
 
 // One key source as the attention kernel sees it.  `base` points at the
@@ -54,7 +55,8 @@ struct AttnLaunch {
   int32_t n_pairs;
   int32_t nh, d, lq;
   int32_t n_qtiles;
-  int32_t n_wg;                    // persistent workgroups (one per CU)
+  int32_t n_wg;                    // persistent workgroups: one per CU, <= kMaxWg (set by the launcher)
+  int32_t n_xcd;                   // XCDs the workgroups are dealt to round-robin (set by the launcher)
   int32_t dtype;                   // ff_dtype
   float scale;                     // 1/sqrt(d)
   int64_t slot_floats;             // floats per partial slot: O [BM][d], m [BM], l [BM]
@@ -105,6 +107,7 @@ struct BcReaders {
 struct BcLaunch {
   int32_t nh, d, T, L;             // heads, head dim, tokens per anchor / per chunk
   int32_t n_anchor, n_chunk, dtype;
+  int32_t n_xcd;                   // XCDs the workgroups are dealt to (set by the launcher)
   float scale;
   int64_t blk_anchor, blk_chunk;   // bytes per anchor / chunk block
   const uint8_t* kv_anchor;
@@ -131,6 +134,10 @@ struct BcLaunch {
   BcReaders readers[kBcMaxAnchors + kBcMaxChunks];   // anchor a at [a], chunk j at [kBcMaxAnchors + j]
 };
 static_assert(sizeof(BcLaunch) <= 4096, "backward launch arguments exceed the kernel argument limit");
+
+// Compute units and XCDs of the current device (hipDeviceAttribute*).
+// Returns 0, or FF_E_HIP when the device cannot be queried.
+int dev_topology(int* n_cu, int* n_xcd);
 
 // Device entry points.  Return 0 on success, FF_E_HIP on a launch error.
 // `prof` (nullable) collects start/stop events when profiling is on.

@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bc_dq_kernel(const BcLaunch 
   __shared__ __attribute__((aligned(1024))) uint8_t kt1[Cfg::kVBytes];
 
   const int n_qt = (b.L + kBlockM - 1) / kBlockM;
-  const int item = xcd_remap(blockIdx.x, gridDim.x);     // q-tiles of one (chunk, head) share an XCD
+  const int item = xcd_remap(blockIdx.x, gridDim.x, b.n_xcd);     // q-tiles of one (chunk, head) share an XCD
   const int qt = item % n_qt;
   const int h = (item / n_qt) % b.nh;
   const int i = item / (n_qt * b.nh);
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kKeyWaves * 64, 1) void bc_dkv_kernel(const BcLaunc
   // Items: chunk sources first (they have the most readers), then anchors.
   const int nkb_c = (b.L + kKeyBlock - 1) / kKeyBlock;
   const int nkb_a = (b.T + kKeyBlock - 1) / kKeyBlock;
-  int item = xcd_remap(blockIdx.x, gridDim.x);     // key blocks of one (source, head) share an XCD
+  int item = xcd_remap(blockIdx.x, gridDim.x, b.n_xcd);     // key blocks of one (source, head) share an XCD
   const bool is_chunk = item < b.n_chunk * b.nh * nkb_c;
   int src, n, h, kb;
   if (is_chunk) {
@@ -523,8 +523,11 @@ void launch_backward(const BcLaunch& b, hipStream_t s, Profiler* prof) {
 
 }  // namespace
 
-int dev_launch_bc_backward(const BcLaunch& b, void* stream, Profiler* prof) {
+int dev_launch_bc_backward(const BcLaunch& b0, void* stream, Profiler* prof) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  BcLaunch b = b0;
+  int n_cu = 0;
+  if (dev_topology(&n_cu, &b.n_xcd) != 0) return FF_E_HIP;
   if (b.d == 64) launch_backward<64>(b, s, prof);
   else launch_backward<128>(b, s, prof);
   return launch_ok();

@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
+#include <mutex>
 #include <vector>
 
 #include "../ff_internal.h"
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch 
   __shared__ __attribute__((aligned(1024))) uint8_t v3[Cfg::kVBytes];
   const LdsBufs lb = {{k0, k1, k2, k3}, {v0, v1, v2, v3}};
   // Consecutive workgroup ids sit on one XCD (shared L2).
-  const int g = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = xcd_remap(blockIdx.x, gridDim.x, a.n_xcd);
   for (int p = 0; p < a.n_pairs; ++p) {
     const PairLaunch& P = a.pair[p];
     const RemSplit rs = rem_split(P.n_items, P.ntiles, a.n_wg);
@@ -697,8 +698,34 @@ __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch 
 
 }  // namespace
 
-int dev_launch_attention(const AttnLaunch& a, void* stream, Profiler* prof) {
+// Compute units and XCDs of each device, queried once per device.
+int dev_topology(int* n_cu, int* n_xcd) {
+  static std::mutex mu;
+  static int cu_of[64] = {}, xcd_of[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return FF_E_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cu_of[dev]) {
+    int cu = 0, xcc = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu < 1)
+      return FF_E_HIP;
+    if (hipDeviceGetAttribute(&xcc, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xcc < 1) xcc = 1;
+    cu_of[dev] = cu;
+    xcd_of[dev] = xcc;
+  }
+  *n_cu = cu_of[dev];
+  *n_xcd = xcd_of[dev];
+  return 0;
+}
+
+int dev_launch_attention(const AttnLaunch& a0, void* stream, Profiler* prof) {
   hipStream_t s = static_cast<hipStream_t>(stream);
+  // One persistent workgroup per CU (at most kMaxWg, the partial slots the
+  // workspace holds per call), dealt to the XCDs as the device reports them.
+  AttnLaunch a = a0;
+  int n_cu = 0;
+  if (dev_topology(&n_cu, &a.n_xcd) != 0) return FF_E_HIP;
+  a.n_wg = n_cu < kMaxWg ? n_cu : kMaxWg;
   if (a.dtype == FF_F32) {
     Timed tm(prof, kAttn, s);
     dim3 grid(unsigned((int64_t(a.lq) * a.nh + 63) / 64), unsigned(a.n_pairs));

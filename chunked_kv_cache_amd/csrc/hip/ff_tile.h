@@ -84,11 +84,13 @@ __device__ __forceinline__ void wait_dma_but() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-__device__ __forceinline__ int xcd_remap(int b, int nb) {
-  // Blocks are dealt to the 8 XCDs round-robin; give each XCD a contiguous
+__device__ __forceinline__ int xcd_remap(int b, int nb, int nx) {
+  // Blocks are dealt to the nx XCDs round-robin; give each XCD a contiguous
   // range of work items so that query tiles sharing a head's K/V share an L2.
-  const int x = b & 7, idx = b >> 3;
-  const int per = nb >> 3, rem = nb & 7;
+  // XCD x receives the blocks b = x (mod nx): per or per + 1 of them, mapped
+  // to one run of consecutive items (a bijection on [0, nb)).
+  const int x = b % nx, idx = b / nx;
+  const int per = nb / nx, rem = nb % nx;
   return x * per + (x < rem ? x : rem) + idx;
 }
 

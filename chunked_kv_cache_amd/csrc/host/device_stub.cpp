@@ -77,6 +77,11 @@ int ffstub_last_segments(int p, const void* ws, long long* offsets, int* n_token
   *ntiles = P.ntiles;
   return P.seg.nseg;
 }
+// Partial-slot region of pair p of the last attention launch, as a byte
+// offset from ws.
+long long ffstub_last_part(int p, const void* ws) {
+  return reinterpret_cast<const char*>(ff::g_last_attn.pair[p].part) - static_cast<const char*>(ws);
+}
 int ffstub_last_attn_pairs(int* n_wg) {
   *n_wg = ff::g_last_attn.n_wg;
   return ff::g_last_attn.n_pairs;

@@ -65,6 +65,9 @@ bool shape_ok(const ff_shape* s, int S, int H) {
   return true;
 }
 
+// Partial slots of one call: two per persistent workgroup.
+size_t part_region_bytes(size_t part_slot) { return size_t(kMaxWg) * 2 * part_slot; }
+
 struct Layout {
   size_t anchor_off, anchor_block, slot_off, slot_block, part_off, part_slot, total;
   int n_anchor, n_chunk;
@@ -81,11 +84,12 @@ Layout layout_of(const ff_shape* s, int S, int H) {
   L.slot_block = align_up(2 * nh * lq * d * esz);
   L.anchor_off = 0;
   L.slot_off = L.anchor_off + size_t(L.n_anchor) * L.anchor_block;
-  // Stream-K partial slots (bf16 path): 2 per workgroup per call that a
-  // grouped launch can hold (one call per stage).
+  // Split-item partial slots (bf16 path): 2 per workgroup, in one region per
+  // stage and one for planner calls, so that calls of different stages (or a
+  // planner call) may run concurrently on different streams.
   L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(kBlockM) * (d + 2) * 4) : 0;
   L.part_off = L.slot_off + size_t(S) * size_t(H + 1) * L.slot_block;
-  L.total = L.part_off + size_t(std::min(S, kMaxPairs)) * size_t(kCUs) * 2 * L.part_slot;
+  L.total = L.part_off + size_t(S + 1) * part_region_bytes(L.part_slot);
   return L;
 }
 
@@ -236,7 +240,6 @@ void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_so
   a->d = c->shape.head_dim;
   a->lq = int32_t(lq);
   a->n_qtiles = int32_t((lq + kBlockM - 1) / kBlockM);
-  a->n_wg = kCUs;
   a->dtype = c->shape.dtype;
   a->scale = float(1.0 / std::sqrt(double(c->shape.head_dim)));
   a->slot_floats = int64_t(c->part_slot_bytes / 4);
@@ -249,8 +252,9 @@ void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_so
     pl.lk = plans[p].key_tokens;
     pl.ntiles = pl.seg.tile_start[pl.seg.nseg];
     pl.n_items = a->nh * a->n_qtiles;
+    const size_t region = ks[p] < 0 ? size_t(c->S) : size_t(ks[p]);     // stage k, or the planner's
     pl.part = c->part_slot_bytes
-                  ? reinterpret_cast<float*>(c->ws + c->part_off + size_t(p) * size_t(kCUs) * 2 * c->part_slot_bytes)
+                  ? reinterpret_cast<float*>(c->ws + c->part_off + region * part_region_bytes(c->part_slot_bytes))
                   : nullptr;
   }
 }
@@ -507,6 +511,43 @@ ff_status ff_stage_next(const ff_ctx* c, int stage, int* next_chunk) {
   return FF_OK;
 }
 
+ff_status ff_clip_layout(const ff_shape* shape, int n_stages, ff_clip_counts* out) {
+  if (!out || !shape_ok(shape, n_stages, 1)) return FF_E_INVAL;
+  const Layout L = layout_of(shape, n_stages, 1);
+  out->n_anchors = L.n_anchor;
+  out->n_chunks = L.n_chunk;
+  out->n_planner_blocks = (L.n_anchor + shape->planner_latents - 1) / shape->planner_latents;
+  out->n_diagonals = L.n_chunk + n_stages - 1;
+  return FF_OK;
+}
+
+ff_status ff_planner_block(const ff_shape* shape, int block, int* first_anchor, int* n_anchors) {
+  if (!first_anchor || !n_anchors || !shape_ok(shape, 1, 1)) return FF_E_INVAL;
+  const int na = layout_of(shape, 1, 1).n_anchor, bp = shape->planner_latents;
+  if (block < 0 || block >= (na + bp - 1) / bp) return FF_E_RANGE;
+  *first_anchor = block * bp;
+  *n_anchors = std::min(bp, na - block * bp);
+  return FF_OK;
+}
+
+// The anti-diagonal wavefront: diagonal t runs (t-k, k) for every stage k
+// whose chunk t-k exists.
+ff_status ff_wavefront(const ff_shape* shape, int n_stages, int t, int* n_pairs, int* chunks, int* stages) {
+  if (!n_pairs || !chunks || !stages || !shape_ok(shape, n_stages, 1)) return FF_E_INVAL;
+  const int nc = layout_of(shape, n_stages, 1).n_chunk;
+  if (t < 0 || t > nc + n_stages - 2) return FF_E_RANGE;
+  int n = 0;
+  for (int k = 0; k < n_stages; ++k) {
+    const int i = t - k;
+    if (i < 0 || i >= nc) continue;
+    chunks[n] = i;
+    stages[n] = k;
+    ++n;
+  }
+  *n_pairs = n;
+  return FF_OK;
+}
+
 ff_status ff_stage_bank_rewind(ff_ctx* c, int stage) {
   if (!c) return FF_E_INVAL;
   if (stage < 0 || stage >= c->S) return FF_E_RANGE;
@@ -593,7 +634,7 @@ BcLayout bc_layout_of(const ff_shape* s) {
   L.gg_chunk = take(size_t(L.n_chunk) * L.blk_chunk);
   L.stats = take(size_t(L.n_chunk) * nh * lq * 8);
   L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(kBlockM) * (d + 2) * 4) : 0;
-  L.part = take(size_t(kMaxPairs) * size_t(kCUs) * 2 * L.part_slot);
+  L.part = take(size_t(kMaxPairs) * part_region_bytes(L.part_slot));
   L.total = off;
   return L;
 }
@@ -740,7 +781,6 @@ ff_status ff_bc_forward(ff_bc* b, const void* Ka, const void* Va, const void* Q,
     a.d = b->shape.head_dim;
     a.lq = int32_t(b->Lq);
     a.n_qtiles = int32_t((b->Lq + kBlockM - 1) / kBlockM);
-    a.n_wg = kCUs;
     a.dtype = b->shape.dtype;
     a.scale = float(1.0 / std::sqrt(double(b->shape.head_dim)));
     a.slot_floats = int64_t(b->part_slot / 4);
@@ -767,7 +807,7 @@ ff_status ff_bc_forward(ff_bc* b, const void* Ka, const void* Va, const void* Q,
       pl.lk = int32_t(int64_t(c.na) * b->T + int64_t(c.nj) * b->Lq);
       pl.ntiles = tiles;
       pl.n_items = a.nh * a.n_qtiles;
-      pl.part = b->part_slot ? reinterpret_cast<float*>(b->ws + b->part + size_t(p) * size_t(kCUs) * 2 * b->part_slot)
+      pl.part = b->part_slot ? reinterpret_cast<float*>(b->ws + b->part + size_t(p) * part_region_bytes(b->part_slot))
                              : nullptr;
     }
     if (dev_launch_attention(a, stream, prof) != 0) return FF_E_HIP;

@@ -39,6 +39,10 @@ class ff_key_sources(ctypes.Structure):
                 ("key_latents", ctypes.c_int32)]
 
 
+class ff_clip_counts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_anchors", "n_chunks", "n_planner_blocks", "n_diagonals")]
+
+
 class ff_kernel_times(ctypes.Structure):
     _fields_ = [("attn_launches", ctypes.c_int64), ("attn_ms", ctypes.c_double),
                 ("merge_launches", ctypes.c_int64), ("merge_ms", ctypes.c_double),
@@ -75,6 +79,10 @@ _SIGS = {
     "ff_key_plan": (_I, [_VP, _I, _I, ctypes.POINTER(ff_key_sources)]),
     "ff_stage_next": (_I, [_VP, _I, ctypes.POINTER(_I)]),
     "ff_stage_bank_rewind": (_I, [_VP, _I]),
+    "ff_clip_layout": (_I, [ctypes.POINTER(ff_shape), _I, ctypes.POINTER(ff_clip_counts)]),
+    "ff_planner_block": (_I, [ctypes.POINTER(ff_shape), _I, ctypes.POINTER(_I), ctypes.POINTER(_I)]),
+    "ff_wavefront": (_I, [ctypes.POINTER(ff_shape), _I, _I, ctypes.POINTER(_I), ctypes.POINTER(_I),
+                          ctypes.POINTER(_I)]),
     "ff_profile_enable": (_I, [_VP, _I]),
     "ff_profile_read": (_I, [_VP, ctypes.POINTER(ff_kernel_times)]),
     "ff_bc_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ff_shape), _I]),
@@ -227,6 +235,28 @@ def ff_stage_next(ctx, stage, L=None) -> int:
 def ff_stage_bank_rewind(ctx, stage, L=None) -> None:
     L = L or lib()
     _check(L.ff_stage_bank_rewind(ctx, stage), L)
+
+
+def ff_clip_layout(shape: ff_shape, n_stages: int = 1, L=None) -> dict:
+    L = L or lib()
+    out = ff_clip_counts()
+    _check(L.ff_clip_layout(ctypes.byref(shape), n_stages, ctypes.byref(out)), L)
+    return {f: getattr(out, f) for f, _ in ff_clip_counts._fields_}
+
+
+def ff_planner_block(shape: ff_shape, block: int, L=None):
+    L = L or lib()
+    first, n = _I(), _I()
+    _check(L.ff_planner_block(ctypes.byref(shape), block, ctypes.byref(first), ctypes.byref(n)), L)
+    return list(range(first.value, first.value + n.value))
+
+
+def ff_wavefront(shape: ff_shape, n_stages: int, t: int, L=None):
+    L = L or lib()
+    n = _I()
+    chunks, stages = (_I * n_stages)(), (_I * n_stages)()
+    _check(L.ff_wavefront(ctypes.byref(shape), n_stages, t, ctypes.byref(n), chunks, stages), L)
+    return [(chunks[j], stages[j]) for j in range(n.value)]
 
 
 def ff_profile_enable(ctx, on: bool, L=None) -> None:

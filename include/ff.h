@@ -21,9 +21,20 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
  *    enqueue kernels on it and return without synchronising; buffers must stay
  *    alive until the stream has passed them.
+ *  - Streams and one renderer context: the calls of one stage, and the
+ *    planner calls, must be ordered on one stream (or by events), as the
+ *    order contract already makes them depend on each other.  Calls of
+ *    different stages may run concurrently on different streams: each stage
+ *    (and the planner) has its own bank slots and its own split-item partial
+ *    region.  The caller orders a call (i, k) after (i, k-1) and after the
+ *    publish of every anchor it reads.  A block-causal context's calls share
+ *    its whole workspace and must all be ordered on one stream.
  *  - The library allocates no device memory.  All device state (anchor bank,
- *    stage banks, split-K partials) lives in one caller-owned workspace of
+ *    stage banks, split-item partials) lives in one caller-owned workspace of
  *    ff_workspace_bytes() bytes, 256-byte aligned, which must outlive the ctx.
+ *  - The context belongs to the device that is current when its calls are
+ *    made; the attention's persistent grid takes that device's CU and XCD
+ *    counts (queried once per device).
  *  - Every call validates all arguments and the state contract before it
  *    enqueues anything.  A call that returns an error other than FF_E_HIP has
  *    enqueued nothing and changed no state.  FF_E_HIP means a HIP launch
@@ -115,7 +126,8 @@ typedef struct {
 
 /* Bytes of device workspace for a context with n_stages banks of history H.
  * 0 if the shape is unsupported.  Layout: anchor bank (every anchor of the
- * clip), S*(H+1) stage-bank slots, split-K partials.                          */
+ * clip), S*(H+1) stage-bank slots, split-item partials (one region per stage
+ * and one for planner calls).                                               */
 size_t ff_workspace_bytes(const ff_shape* shape, int n_stages, int history);
 
 /* ff_stage_bank_create -- [S] "how it works", Eq. (2): one history bank B_k
@@ -185,6 +197,42 @@ ff_status ff_key_plan(const ff_ctx* ctx, int chunk, int stage, ff_key_sources* o
 
 /* Next chunk id stage k expects (== number of chunks it has published). */
 ff_status ff_stage_next(const ff_ctx* ctx, int stage, int* next_chunk);
+
+/* Counts that follow from a shape.  [S] "how it differs": 81 latents give 9
+ * anchors at 0, 10, .., 80 (3 planner blocks of B_P = 3) and 27 renderer
+ * chunks of B_R = 3 latents; [S] "how it works": with one denoising stage
+ * per pipeline step the renderer runs as an anti-diagonal wavefront, whose
+ * N_c + S - 1 diagonals hold every (chunk, stage) call once.               */
+typedef struct {
+  int32_t n_anchors;         /* ceil(n_latents / Delta)                      */
+  int32_t n_chunks;          /* N_c = n_latents / B_R                        */
+  int32_t n_planner_blocks;  /* ceil(n_anchors / B_P)                        */
+  int32_t n_diagonals;       /* N_c + n_stages - 1                           */
+} ff_clip_counts;
+
+/* ff_clip_layout -- the counts above for `shape` with n_stages stages.
+ * Host only; FF_E_INVAL for an unsupported shape or n_stages outside 1..64. */
+ff_status ff_clip_layout(const ff_shape* shape, int n_stages, ff_clip_counts* out);
+
+/* ff_planner_block -- anchors of planner block `block`: first_anchor ..
+ * first_anchor + n_anchors - 1 ([S] "how it differs": anchors are generated
+ * B_P at a time, in order; the last block may be shorter).  Host only;
+ * FF_E_RANGE for a block outside the clip.                                  */
+ff_status ff_planner_block(const ff_shape* shape, int block, int* first_anchor, int* n_anchors);
+
+/* ff_wavefront -- the renderer calls of anti-diagonal t of the wavefront
+ * schedule: the pairs (chunk t-k, stage k) for 0 <= k < n_stages with
+ * 0 <= t-k < N_c, in ascending stage order, written to chunks[] and
+ * stages[] (host arrays of at least n_stages entries), *n_pairs of them.
+ * [S] "how it works": the renderer's same-stage dependency lets the chunks
+ * sit at different stages at once, one stage per pipeline step; [A]
+ * abstract: once chunk i finishes stage k, its stage-k cache is ready for
+ * chunk i+1.  Every dependency of a call on diagonal t -- (i-1, k) and
+ * (i, k-1) -- lies on diagonal t-1, so the calls of one diagonal are
+ * independent (one per stage: one ff_render_attend_grouped launch), and
+ * t = 0 .. N_c+n_stages-2 in order runs every call of the clip legally.
+ * Host only; FF_E_RANGE for t outside that range.                          */
+ff_status ff_wavefront(const ff_shape* shape, int n_stages, int t, int* n_pairs, int* chunks, int* stages);
 
 /* ff_stage_bank_rewind -- undo the newest publish of stage k (retry of that
  * chunk, or a steady-state replay).  Exact because the ring keeps H+1 slots:

@@ -27,6 +27,14 @@ LSE_TOL = {"bf16": 2e-3, "f32": 1e-4}
 RELF_TOL = {"bf16": 1e-2, "f32": 1e-5}     # relative Frobenius (diagnostic gate)
 
 
+def wavefront(case: "Case"):
+    """The library's own anti-diagonal schedule (ff_wavefront), which drives the
+    GPU rollouts; a CPU test pins it to the oracle's schedule."""
+    shape = case.shape()
+    n = ff.ff_clip_layout(shape, case.S)["n_diagonals"]
+    return [ff.ff_wavefront(shape, case.S, t) for t in range(n)]
+
+
 def to_device(x: np.ndarray, dtype: str):
     import torch
     if dtype == "bf16":

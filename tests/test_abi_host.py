@@ -394,3 +394,88 @@ def test_planner_shape_limits():
                dict(planner_history=9, w_ctx=30)):                   # 30 planner sources > 24
         bad = ff.make_shape(n_heads=2, head_dim=64, tokens_per_latent=16, **kw)
         assert ff.ff_workspace_bytes(bad, 4, 5, L=L) == 0, kw
+
+
+# --------------------------------------------------------------------------
+# The library's own rollout driver pieces: wavefront schedule, planner blocks,
+# clip counts (host-only calls of libff.so), pinned to the oracle
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 2, 3, 4])
+@pytest.mark.parametrize("n_latents", [81, 261])
+def test_wavefront_schedule_matches_oracle(n_latents, S):
+    L = ff.load(ff.LIB_PATH)
+    shape = ff.make_shape(n_heads=2, head_dim=128, tokens_per_latent=16, n_latents=n_latents)
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=128, n_latents=n_latents, n_stages=S)
+    counts = ff.ff_clip_layout(shape, S, L=L)
+    assert counts == {"n_anchors": orc.n_anchors(cfg), "n_chunks": orc.n_chunks(cfg),
+                      "n_planner_blocks": len(orc.planner_blocks(cfg)),
+                      "n_diagonals": orc.n_chunks(cfg) + S - 1}
+    sched = [ff.ff_wavefront(shape, S, t, L=L) for t in range(counts["n_diagonals"])]
+    assert sched == orc.schedule(cfg)
+    calls = [p for d in sched for p in d]
+    assert orc.is_legal_order(cfg, calls)
+    assert sorted(calls) == [(i, k) for i in range(orc.n_chunks(cfg)) for k in range(S)]
+    for t in (-1, counts["n_diagonals"]):
+        with pytest.raises(ff.FFError) as e:
+            ff.ff_wavefront(shape, S, t, L=L)
+        assert e.value.status == ff.FF_E_RANGE
+
+
+@pytest.mark.parametrize("n_latents", [3, 42, 81, 261])
+def test_planner_blocks_match_oracle(n_latents):
+    L = ff.load(ff.LIB_PATH)
+    shape = ff.make_shape(n_heads=2, head_dim=128, tokens_per_latent=16, n_latents=n_latents)
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=128, n_latents=n_latents)
+    n = ff.ff_clip_layout(shape, L=L)["n_planner_blocks"]
+    assert [ff.ff_planner_block(shape, b, L=L) for b in range(n)] == orc.planner_blocks(cfg)
+    with pytest.raises(ff.FFError) as e:
+        ff.ff_planner_block(shape, n, L=L)
+    assert e.value.status == ff.FF_E_RANGE
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_wavefront_drives_the_order_contract(S):
+    """The product schedule, fed to grouped calls, passes the library's own
+    order checks for a whole 261-latent clip (348 calls at S = 4)."""
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=128, n_latents=261, n_stages=S)
+    hc = HostCtx(cfg)
+    try:
+        _publish_anchors(hc)
+        n = ff.ff_clip_layout(hc.shape, S, L=hc.L)["n_diagonals"]
+        calls = 0
+        for t in range(n):
+            diag = ff.ff_wavefront(hc.shape, S, t, L=hc.L)
+            m = len(diag)
+            ff.ff_render_attend_grouped(hc.ctx, [i for i, _ in diag], [k for _, k in diag], [FAKE] * m,
+                                        [FAKE] * m, [FAKE] * m, [FAKE] * m, L=hc.L)
+            calls += m
+        assert calls == 87 * S
+        for k in range(S):
+            assert ff.ff_stage_next(hc.ctx, k, L=hc.L) == 87
+    finally:
+        hc.close()
+
+
+def test_partial_regions_are_per_stage():
+    """Split-item partials: stage k uses region k and planner calls region S, so
+    calls of different stages never share partial slots (concurrent streams)."""
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=128, n_stages=3)
+    hc = HostCtx(cfg)
+    f = hc.L.ffstub_last_part
+    f.restype = ctypes.c_longlong
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p]
+    try:
+        _, slot_block, slot_off = _layout(cfg)
+        part_off = slot_off + 3 * 6 * slot_block
+        part_slot = (256 * 130 * 4 + 255) // 256 * 256
+        region = 256 * 2 * part_slot
+        assert hc.need == part_off + 4 * region
+        _publish_anchors(hc)
+        for t in range(3):
+            diag = ff.ff_wavefront(hc.shape, 3, t, L=hc.L)
+            m = len(diag)
+            ff.ff_render_attend_grouped(hc.ctx, [i for i, _ in diag], [k for _, k in diag], [FAKE] * m,
+                                        [FAKE] * m, [FAKE] * m, [FAKE] * m, L=hc.L)
+            assert [f(p, hc.ws) for p in range(m)] == [part_off + k * region for _, k in diag]
+    finally:
+        hc.close()

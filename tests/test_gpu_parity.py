@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 import oracle as orc
-from ffharness import Case, Pair
+from ffharness import Case, Pair, wavefront
 
 pytestmark = pytest.mark.gpu
 
@@ -20,7 +20,7 @@ def _rollout(case, grouped=False, rows=None, control_from=None, every=1, max_dia
     pr = Pair(case)
     try:
         pr.publish_anchors()
-        diags = orc.schedule(case.cfg)
+        diags = wavefront(case)
         if max_diag is not None:
             diags = diags[:max_diag]
         for t, diag in enumerate(diags):
@@ -87,7 +87,7 @@ def test_grouped_bits_equal_single_calls():
         try:
             pr.publish_anchors()
             res = {}
-            for diag in orc.schedule(case.cfg)[:12]:
+            for diag in wavefront(case)[:12]:
                 host = [pr.gen(i, k) for i, k in diag]
                 from ffharness import to_device
                 from chunked_kv_cache_amd import ff
@@ -137,7 +137,7 @@ def _planner_rollout(case, steps=2, rows=None, render_diags=0, control=True):
             for step in range(steps):
                 pr.plan_step(b, step, publish=False, rows=rows, control=control and b > 0 and step == 0)
             pr.plan_step(b, steps, publish=True, rows=rows)
-        for diag in orc.schedule(case.cfg)[:render_diags]:
+        for diag in wavefront(case)[:render_diags]:
             pr.step(diag, grouped=True, rows=rows)
         return pr.stats
     finally:
@@ -159,7 +159,7 @@ def test_planner_short_blocks(n_latents):
     case = Case(T=16, nh=2, d=128, n_latents=n_latents, S=2)
     n_blocks = len(orc.planner_blocks(case.cfg))
     st = _planner_rollout(case, render_diags=3)
-    assert st.calls == 3 * n_blocks + sum(len(d) for d in orc.schedule(case.cfg)[:3])
+    assert st.calls == 3 * n_blocks + sum(len(d) for d in wavefront(case)[:3])
 
 
 @pytest.mark.parametrize("h_p", [6, 2])
@@ -222,7 +222,7 @@ def test_480p_rollout_grouped_full_size():
     pr = Pair(case, device_bank_check=True)
     try:
         pr.publish_anchors()
-        for t, diag in enumerate(orc.schedule(case.cfg)):
+        for t, diag in enumerate(wavefront(case)):
             pr.step(diag, grouped=True, rows=rows, control=(t == 12))
             print(f"  diagonal {t}: {len(diag)} pairs ok", flush=True, file=sys.stderr)
         assert pr.stats.calls == 108 and pr.stats.bank_checks == 108

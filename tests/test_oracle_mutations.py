@@ -38,6 +38,14 @@ MUTATIONS = {
     "planner_own_dropped": ("            ks.append(np.asarray(K))\n            vs.append(np.asarray(V))\n", ""),
     "planner_no_order_check": ("        for x in range(b):\n            for a in blocks[x]:", "        for x in range(0):\n            for a in blocks[x]:"),
     "planner_publish_shifted": ("self.publish_anchors(blocks[b][0], K, V)", "self.publish_anchors(blocks[b][-1], K, V)"),
+    # the sampled-row path of the full-size GPU comparisons
+    "rows_select_keys": ("O, LSE = attention(np.asarray(Q)[np.asarray(rows)], K, V, scale)",
+                         "O, LSE = attention(Q, np.asarray(K)[np.asarray(rows)], np.asarray(V)[np.asarray(rows)], "
+                         "scale)"),
+    "rows_sorted_silently": ("O, LSE = attention(np.asarray(Q)[np.asarray(rows)], K, V, scale)",
+                             "O, LSE = attention(np.asarray(Q)[np.sort(np.asarray(rows))], K, V, scale)"),
+    "render_rows_ignored": ("                O, LSE = attention_rows(Q, Kc, Vc, cfg.scale, rows)\n        # Tail_H",
+                            "                O, LSE = attention(Q, Kc, Vc, cfg.scale)\n        # Tail_H"),
     # block-causal forward and gradients (oracle/block_causal.py)
     "bc_window_long": ("hist = list(range(max(0, i - cfg.history), i))",
                        "hist = list(range(max(0, i - cfg.history - 1), i))", BC),

@@ -462,3 +462,70 @@ def test_planner_each_source_reaches_the_output(target):
     Q[:, 0] = 400.0 * eye[1]
     O, _ = ro.plan_attend(b, Q, Kown, Vown)
     assert np.all(np.abs(O[:, 0, :] - 1.0 * 11.0) > 1.0)
+
+
+# --------------------------------------------------------------------------
+# The sampled-row path (attention_rows, render_attend / plan_attend with rows=)
+# that every full-size GPU parity case compares against
+# --------------------------------------------------------------------------
+ROW_SETS = {
+    "sorted": [0, 3, 4, 17, 31, 32],
+    "unsorted": [31, 2, 17, 0, 9],
+    "singleton": [13],
+    "repeated": [5, 5, 30],
+}
+
+
+@pytest.mark.parametrize("rows", sorted(ROW_SETS))
+def test_attention_rows_vs_sdpa_on_the_rows(rows):
+    """attention_rows equals torch SDPA (float64, CPU) on exactly the chosen
+    query rows, in the order given, and equals the full call restricted to them."""
+    r = ROW_SETS[rows]
+    Lq, Lk, nh, d = 33, 70, 3, 16
+    Q, K, V = _rand((Lq, nh, d), 11), _rand((Lk, nh, d), 12), _rand((Lk, nh, d), 13)
+    scale = 1.0 / math.sqrt(d)
+    O, LSE = orc.attention_rows(Q, K, V, scale, r)
+    assert O.shape == (len(r), nh, d) and LSE.shape == (nh, len(r))
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x.transpose(1, 0, 2)))[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(t(Q[r]), t(K), t(V))[0].numpy().transpose(1, 0, 2)
+    np.testing.assert_allclose(O, ref, rtol=0, atol=1e-12)
+    for h in range(nh):
+        s = Q[r, h] @ K[:, h].T * scale
+        np.testing.assert_allclose(LSE[h], logsumexp(s, axis=1), rtol=0, atol=1e-12)
+    O_full, LSE_full = orc.attention(Q, K, V, scale)
+    np.testing.assert_allclose(O, O_full[r], rtol=0, atol=1e-13)        # BLAS rounding order only
+    np.testing.assert_allclose(LSE, LSE_full[:, r], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("rows", ["sorted", "unsorted", "singleton"])
+def test_render_attend_rows_equal_full_call(rows):
+    """Two rollouts in lockstep: the rows= call returns the full call's O rows
+    and LSE columns for every call of two stages, and leaves the same banks."""
+    cfg = cfg81(n_stages=2)
+    r = [x % (3 * cfg.tokens_per_latent) for x in ROW_SETS[rows]]
+    full, part = orc.Rollout(cfg), orc.Rollout(cfg)
+    _publish_all_anchors(full, cfg)
+    _publish_all_anchors(part, cfg)
+    for diag in orc.schedule(cfg)[:12]:
+        for i, k in diag:
+            q, kk, vv = (syn.as_f64(x, "f32") for x in syn.chunk_qkv(
+                T=cfg.tokens_per_latent, n_heads=cfg.n_heads, head_dim=cfg.head_dim, chunk=i, stage=k, dtype="f32"))
+            O, LSE = full.render_attend(i, k, q, kk, vv)
+            Or, LSEr = part.render_attend(i, k, q, kk, vv, rows=r)
+            np.testing.assert_allclose(Or, O[r], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(LSEr, LSE[:, r], rtol=0, atol=1e-13)
+            assert part.bank_tail(k)[0] == full.bank_tail(k)[0]
+
+
+def test_plan_attend_rows_equal_full_call():
+    cfg = cfg81(n_latents=261, n_stages=1)
+    T = cfg.tokens_per_latent
+    r = [11, 0, 7]
+    full, part = orc.Rollout(cfg), orc.Rollout(cfg)
+    for b, blk in enumerate(orc.planner_blocks(cfg)):
+        q, kk, vv = (syn.as_f64(x, "f32") for x in syn.planner_qkv(
+            T=T, n_heads=cfg.n_heads, head_dim=cfg.head_dim, block=b, step=0, n_latents=len(blk), dtype="f32"))
+        O, LSE = full.plan_attend(b, q, kk, vv, publish=True)
+        Or, LSEr = part.plan_attend(b, q, kk, vv, publish=True, rows=r)
+        np.testing.assert_allclose(Or, O[r], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(LSEr, LSE[:, r], rtol=0, atol=1e-13)
