@@ -184,14 +184,21 @@ def main():
     torch.cuda.synchronize()
 
     ff.ff_profile_enable(ctx, True)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    clocks = ClockSampler().start()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for j in range(args.steps):
+        events[j][0].record()
         one_step(steps_done + j)
+        events[j][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    clock_info = clocks.stop()
     prof = ff.ff_profile_read(ctx)
     ff.ff_profile_enable(ctx, False)
+    steps_ms = step_stats(events)
 
     ms_per_step = wall * 1e3 / args.steps
     tflops = flops * args.steps / wall / 1e12
@@ -201,7 +208,8 @@ def main():
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
     pub_gbps = pub_bytes / (pub_ms * 1e-3) / 1e9
     log(f"attention kernel {attn_ms:.3f} ms ({attn_tflops:.1f} TFLOP/s), merge {merge_ms:.3f} ms, "
-        f"publish {pub_ms * 1e3:.1f} us ({pub_gbps:.0f} GB/s), step {ms_per_step:.3f} ms")
+        f"publish {pub_ms * 1e3:.1f} us ({pub_gbps:.0f} GB/s), step {ms_per_step:.3f} ms "
+        f"(median {steps_ms['median']:.3f}, min {steps_ms['min']:.3f}); clocks {clock_info}")
 
     if args.calibration_copy:
         calibration_copy()
@@ -228,6 +236,8 @@ def main():
                    "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "chunk_steps_per_s": round(args.steps / wall, 2),
+        "step_ms": steps_ms,
+        "clocks": clock_info,
         "attention_kernel_ms": round(attn_ms, 4),
         "merge_kernel_ms": round(merge_ms, 4),
         "publish_kernel_us": round(pub_ms * 1e3, 2),
@@ -240,6 +250,66 @@ def main():
     }
     print(json.dumps(out), flush=True)
     banks.close()
+
+
+class ClockSampler:
+    """Samples the GPU's current shader and memory clock levels (the entries
+    marked '*' in the driver's pp_dpm_sclk / pp_dpm_mclk files) every 20 ms
+    in a thread while the timed region runs; reports their range and mode."""
+
+    def __init__(self):
+        import glob
+        self.files = {k: sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{k}")) for k in ("sclk", "mclk")}
+        self.samples = {"sclk": [], "mclk": []}
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _current_mhz(path):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return int("".join(ch for ch in line.split(":", 1)[1] if ch.isdigit()))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k, paths in self.files.items():
+                vals = [v for v in (self._current_mhz(p) for p in paths) if v]
+                if vals:
+                    self.samples[k].append(max(vals))
+            self._stop.wait(0.02)
+
+    def start(self):
+        import threading
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def stop(self):
+        if self._thread:
+            self._stop.set()
+            self._thread.join()
+        out = {}
+        for k, v in self.samples.items():
+            if v:
+                out[f"{k}_mhz"] = {"min": min(v), "max": max(v), "mode": max(set(v), key=v.count),
+                                   "samples": len(v)}
+            else:
+                out[f"{k}_mhz"] = None
+        out["source"] = "pp_dpm_sclk / pp_dpm_mclk current level, sampled every 20 ms" \
+            if any(self.files.values()) else "not readable on this host"
+        return out
+
+
+def step_stats(events):
+    """Median / min / mean of per-step device times from (start, end) event pairs."""
+    ms = sorted(a.elapsed_time(b) for a, b in events)
+    return {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4), "mean": round(sum(ms) / len(ms), 4),
+            "n": len(ms)}
 
 
 def calibration_copy():
@@ -603,6 +673,55 @@ def cpu_baseline_planner(host_qkv, block, T, nh, d, n_heads_sample, n_latents):
                       f"{nh} heads: {flops / 1e9:.0f} GFLOP in {dt:.1f} s"}
 
 
+def _host_info():
+    """CPU model and the BLAS the oracle's numpy runs on (threadpoolctl)."""
+    import numpy  # noqa: F401  (loads the BLAS so threadpoolctl can see it)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api')} {libs[0].get('version')} ({libs[0].get('threading_layer')})"
+    except Exception:
+        pass
+    return {"cpu_model": model, "blas": blas, "affinity_cores": len(os.sched_getaffinity(0))}
+
+
+def tiny_rollout_one_thread():
+    """The float64 oracle's whole tiny rollout (fp32 inputs: T = 16, 2 heads,
+    d = 64, 81 latents, 9 anchors, 27 chunks x 4 stages = 108 calls) on one
+    BLAS thread: seconds and GFLOP/s."""
+    import oracle as orc
+    import synthetic as syn
+    from threadpoolctl import threadpool_limits
+    cfg = orc.FFConfig(tokens_per_latent=16, n_heads=2, head_dim=64)
+    with threadpool_limits(limits=1, user_api="blas"):
+        t0 = time.perf_counter()
+        ro = orc.Rollout(cfg)
+        for blk in orc.planner_blocks(cfg):
+            K, V = syn.anchor_kv(T=16, n_heads=2, head_dim=64, anchors=blk, dtype="f32")
+            ro.publish_anchors(blk[0], syn.as_f64(K, "f32"), syn.as_f64(V, "f32"))
+        flops = 0.0
+        for diag in orc.schedule(cfg):
+            for i, k in diag:
+                q, kk, vv = (syn.as_f64(x, "f32") for x in syn.chunk_qkv(T=16, n_heads=2, head_dim=64, chunk=i,
+                                                                          stage=k, dtype="f32"))
+                nk = sum(16 if kind == "anchor" else 48 for kind, _ in ro.key_sources(i, k))
+                ro.render_attend(i, k, q, kk, vv)
+                flops += 4.0 * 48 * nk * 64 * 2
+        dt = time.perf_counter() - t0
+    return {"seconds": round(dt, 3), "gflops": round(flops / dt / 1e9, 3), "calls": 108,
+            "what": "float64 oracle, whole tiny fp32 rollout (inputs, Tail_H banks, 108 calls), 1 BLAS thread"}
+
+
 def _threads():
     try:
         from threadpoolctl import threadpool_info
@@ -643,7 +762,9 @@ def cpu_baseline(ctx, host_qkv, chunk, T, nh, d, n_heads_sample, n_latents):
         flops += 4.0 * 3 * T * T * orc.key_latents(cfg, i, cfg.history) * d * n_heads_sample
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 oracle renderer calls for chunks {chunk} and {chunk + 1} (stage 0, 20 key "
-                      f"latents each), {n_heads_sample} of {nh} heads: {flops / 1e9:.0f} GFLOP in {dt:.1f} s"}
+                      f"latents each), {n_heads_sample} of {nh} heads: {flops / 1e9:.0f} GFLOP in {dt:.1f} s",
+            "seconds_per_chunk_step": round(dt / 2 * nh / n_heads_sample, 2),
+            **_host_info(), "tiny_rollout_1_thread": tiny_rollout_one_thread()}
 
 
 if __name__ == "__main__":

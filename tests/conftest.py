@@ -32,3 +32,26 @@ def load_golden(name):
 @pytest.fixture
 def golden():
     return load_golden
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With FF_PARITY_SUMMARY=<path>, write the error statistics of every GPU
+    parity case of the session (max |dO|, relative Frobenius, LSE, control
+    ratio) as a markdown table."""
+    path = os.environ.get("FF_PARITY_SUMMARY")
+    if not path:
+        return
+    try:
+        from ffharness import RECORDS
+    except Exception:
+        return
+    if not RECORDS:
+        return
+    with open(path, "w") as f:
+        f.write("| case | calls | bank checks | max abs dO | max (abs dO / gate) | max rel. Frobenius | "
+                "max abs dLSE | min control ratio |\n")
+        f.write("|---|---|---|---|---|---|---|---|\n")
+        for name, st in RECORDS:
+            ctl = "-" if st.min_control_ratio == float("inf") else f"{st.min_control_ratio:.1f}"
+            f.write(f"| {name} | {st.calls} | {st.bank_checks} | {st.max_abs:.3e} | {st.max_gate_use:.3f} | "
+                    f"{st.max_rel_fro:.3e} | {st.max_lse:.3e} | {ctl} |\n")

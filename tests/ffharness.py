@@ -82,6 +82,7 @@ class Stats:
     max_rel_fro: float = 0.0
     max_lse: float = 0.0
     min_control_ratio: float = math.inf
+    max_gate_use: float = 0.0              # max over calls of (O max-abs error) / (its gate)
     calls: int = 0
     bank_checks: int = 0
 
@@ -236,6 +237,7 @@ class Pair:
         st.max_abs = max(st.max_abs, err)
         st.max_rel_fro = max(st.max_rel_fro, relf)
         st.max_lse = max(st.max_lse, lerr)
+        st.max_gate_use = max(st.max_gate_use, err / tol)
         st.calls += 1
         assert err <= tol, f"O max-abs {err:.3e} > {tol:.3e}"
         assert relf <= RELF_TOL[dt], f"O rel-Frobenius {relf:.3e} > {RELF_TOL[dt]}"
@@ -276,4 +278,17 @@ class Pair:
         self.stats.bank_checks += 1
 
     def close(self):
+        record(self.stats)
         self.banks.close()
+
+
+# Error statistics of every parity case of the session; conftest writes them
+# to the file named by FF_PARITY_SUMMARY (if set) when the session ends.
+RECORDS: List[tuple] = []
+
+
+def record(stats: "Stats", label: Optional[str] = None) -> None:
+    import os
+    name = label or os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    if stats.calls:
+        RECORDS.append((name, stats))

@@ -250,3 +250,177 @@ def test_720p_step_sampled_rows():
               f"control>={pr.stats.min_control_ratio:.1f}x")
     finally:
         pr.close()
+
+
+def test_rewind_and_repeat():
+    """ff_stage_bank_rewind, then the same calls again with new inputs (the
+    steady-state replay the step benchmark uses): O, LSE and every bank after
+    the repeat match the oracle of the state before the first run, and the
+    rollout then continues correctly."""
+    import copy
+    import dataclasses
+
+    from chunked_kv_cache_amd import ff
+    case = Case(T=200, nh=2, d=128, S=2)
+    pr = Pair(case)
+    try:
+        pr.publish_anchors()
+        diags = wavefront(case)
+        for diag in diags[:8]:
+            pr.step(diag, grouped=True)
+        snap = copy.deepcopy(pr.ro)
+        pr.step(diags[8], grouped=True, control=True)
+        for _, k in sorted(diags[8], key=lambda p: -p[1]):
+            ff.ff_stage_bank_rewind(pr.ctx, k)
+        pr.ro = snap
+        pr.case = dataclasses.replace(case, seed=5)          # different inputs for the repeat
+        pr.step(diags[8], grouped=False, control=True)
+        for diag in diags[9:12]:
+            pr.step(diag, grouped=True)
+        assert pr.stats.calls == sum(len(d) for d in diags[:12]) + len(diags[8])
+    finally:
+        pr.close()
+
+
+def test_two_streams_one_stage_each():
+    """Stage 0 on one stream, stage 1 on another, (i, 1) after (i, 0) by an
+    event: calls of different stages overlap on the GPU and use their own
+    partial regions (T = 200: every item is split, so partials are written).
+    Every output matches the oracle; the banks end bit-exact."""
+    import torch
+
+    import synthetic as syn
+    from chunked_kv_cache_amd import ff
+    from ffharness import from_device_f64, to_device
+    case = Case(T=200, nh=2, d=128, S=2)
+    pr = Pair(case)
+    try:
+        pr.publish_anchors()
+        torch.cuda.synchronize()
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        nc = 27
+        keep, outs = {}, {}
+        for i in range(nc):                      # inputs and NaN-filled outputs, all ready before any call
+            for k in (0, 1):
+                keep[(i, k)] = [to_device(x, "bf16") for x in pr.gen(i, k)]
+                outs[(i, k)] = (torch.full_like(keep[(i, k)][0], float("nan")),
+                                torch.full((case.nh, 3 * case.T), float("nan"), dtype=torch.float32,
+                                           device="cuda"))
+        torch.cuda.synchronize()
+        for i in range(nc):
+            for k in (0, 1):
+                dev, (o, l), s = keep[(i, k)], outs[(i, k)], streams[k]
+                if k == 1:
+                    s.wait_event(done0)
+                ff.ff_render_attend(pr.ctx, i, k, dev[0], dev[1], dev[2], o, l, stream=s)
+                if k == 0:
+                    done0 = torch.cuda.Event()
+                    done0.record(s)
+        torch.cuda.synchronize()
+        for i in range(nc):
+            for k in (0, 1):
+                q64, k64, v64 = (syn.as_f64(x, "bf16") for x in pr.gen(i, k))
+                O_ref, L_ref = pr.ro.render_attend(i, k, q64, k64, v64)
+                pr.inputs[(i, k)] = pr.gen(i, k)[1:]
+                o, l = outs[(i, k)]
+                pr._compare(from_device_f64(o), l.cpu().numpy().astype(np.float64), O_ref, L_ref, None, 2e-2)
+        for k in (0, 1):
+            pr.check_bank(k)
+        assert pr.stats.calls == 2 * nc
+    finally:
+        pr.close()
+
+
+def test_65s_rollout_grouped_full_size():
+    """The 65 s rollout at its stated shape: 480p (T = 1560, 12 heads, d = 128),
+    261 latents, 27 anchors in 9 planner blocks, 87 chunks x 4 stages = 348
+    calls in 90 grouped anti-diagonal launches from the library's schedule.
+    Inputs: 8 seeded N(0,1) sets, call (i, k) taking set (i + k) mod 8, so the
+    six chunks one call reads from a bank are all different.  Every call: O
+    and LSE on 16 sampled query rows of heads 0 and 7 against the oracle run on
+    those heads; every stage bank of the diagonal compared bit for bit on the
+    device with the input tensors; an anchor-less control on diagonal 40."""
+    import sys
+
+    import torch
+
+    import synthetic as syn
+    from chunked_kv_cache_amd import ff
+    from ffharness import LSE_TOL, RELF_TOL, TOL, Stats, record
+    T, nh, d, S, P = 1560, 12, 128, 4, 8
+    heads = [0, 7]
+    case = Case(T=T, nh=nh, d=d, n_latents=261, S=S)
+    cfg_o = orc.FFConfig(tokens_per_latent=T, n_heads=len(heads), head_dim=d, n_latents=261, n_stages=S)
+    rows = np.sort(np.random.default_rng(13).choice(3 * T, size=16, replace=False))
+    rows_d = torch.as_tensor(rows, device="cuda")
+    banks = ff.StageBanks(case.shape(), S, 5)
+    banks.workspace.view(torch.int16).fill_(0x7FC0)
+    ro = orc.Rollout(cfg_o)
+    st = Stats()
+    try:
+        pool_dev, pool_f64 = [], []
+        for j in range(P):
+            host = syn.chunk_qkv(T=T, n_heads=nh, head_dim=d, chunk=j, stage=0, seed=3)
+            pool_dev.append([torch.from_numpy(x).view(torch.bfloat16).cuda() for x in host])
+            pool_f64.append([syn.as_f64(x[:, heads], "bf16") for x in host])
+        for b in range(ff.ff_clip_layout(case.shape(), S)["n_planner_blocks"]):
+            blk = ff.ff_planner_block(case.shape(), b)
+            K, V = syn.anchor_kv(T=T, n_heads=nh, head_dim=d, anchors=blk, seed=3)
+            ff.ff_anchor_bank_publish(banks.ctx, blk[0], len(blk), torch.from_numpy(K).view(torch.bfloat16).cuda(),
+                                      torch.from_numpy(V).view(torch.bfloat16).cuda())
+            ro.publish_anchors(blk[0], syn.as_f64(K[:, heads], "bf16"), syn.as_f64(V[:, heads], "bf16"))
+        print("  anchors published", flush=True, file=sys.stderr)
+        outs = [torch.empty((3 * T, nh, d), dtype=torch.bfloat16, device="cuda") for _ in range(S)]
+        lses = [torch.empty((nh, 3 * T), dtype=torch.float32, device="cuda") for _ in range(S)]
+        Ko = torch.empty((5 * 3 * T, nh, d), dtype=torch.bfloat16, device="cuda")
+        Vo = torch.empty_like(Ko)
+        for t, diag in enumerate(wavefront(case)):
+            sets = [(i + k) % P for i, k in diag]
+            for o in outs:
+                o.fill_(float("nan"))
+            ff.ff_render_attend_grouped(banks.ctx, [i for i, _ in diag], [k for _, k in diag],
+                                        [pool_dev[s][0] for s in sets], [pool_dev[s][1] for s in sets],
+                                        [pool_dev[s][2] for s in sets], [outs[k] for _, k in diag],
+                                        [lses[k] for _, k in diag])
+            torch.cuda.synchronize()
+            for (i, k), s in zip(diag, sets):
+                q64, k64, v64 = pool_f64[s]
+                ctl = None
+                if t == 40:
+                    Kc, Vc = ro.gather_keys(i, k, k64, v64)
+                    na = T * len(orc.gamma(cfg_o, i))
+                    ctl, _ = orc.attention(q64[rows], Kc[na:], Vc[na:], cfg_o.scale)
+                O_ref, L_ref = ro.render_attend(i, k, q64, k64, v64, rows=rows)
+                O = outs[k][rows_d][:, heads].float().cpu().numpy().astype(np.float64)
+                L = lses[k][heads][:, rows_d].cpu().numpy().astype(np.float64)
+                assert np.all(np.isfinite(O))
+                err = np.abs(O - O_ref).max()
+                relf = np.linalg.norm(O - O_ref) / np.linalg.norm(O_ref)
+                lerr = np.abs(L - L_ref).max()
+                st.max_abs, st.max_rel_fro, st.max_lse = max(st.max_abs, err), max(st.max_rel_fro, relf), \
+                    max(st.max_lse, lerr)
+                st.max_gate_use = max(st.max_gate_use, err / TOL["bf16"])
+                st.calls += 1
+                assert err <= TOL["bf16"] and relf <= RELF_TOL["bf16"] and lerr <= LSE_TOL["bf16"], \
+                    (i, k, err, relf, lerr)
+                if ctl is not None:
+                    ratio = np.linalg.norm(O - ctl) / max(np.linalg.norm(O - O_ref), 1e-30)
+                    st.min_control_ratio = min(st.min_control_ratio, ratio)
+                    assert ratio >= 10.0, ratio
+                # stage bank k on the device against the pool tensors it must hold
+                ids = ff.ff_bank_tail(banks.ctx, k, Ko, Vo)
+                assert ids == ro.bank_tail(k)[0]
+                L3 = 3 * T
+                for jj, cid in enumerate(ids):
+                    src = pool_dev[(cid + k) % P]
+                    assert torch.equal(Ko[jj * L3:(jj + 1) * L3].view(torch.int16), src[1].view(torch.int16))
+                    assert torch.equal(Vo[jj * L3:(jj + 1) * L3].view(torch.int16), src[2].view(torch.int16))
+                st.bank_checks += 1
+            if t % 10 == 0:
+                print(f"  diagonal {t}: {len(diag)} pairs ok", flush=True, file=sys.stderr)
+        assert st.calls == 348 and st.bank_checks == 348
+        print(f"65 s rollout grouped: max|dO|={st.max_abs:.2e} relF={st.max_rel_fro:.2e} "
+              f"control>={st.min_control_ratio:.1f}x")
+    finally:
+        record(st)
+        banks.close()
