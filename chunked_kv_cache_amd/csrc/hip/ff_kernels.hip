@@ -26,9 +26,14 @@
 namespace ff {
 namespace {
 
-// Lazy rescale threshold (base-2 units): the running max is only raised when
-// a tile exceeds it by more than this, so p = 2^(s - m) stays <= 2^8.
-constexpr float kRescaleTau = 8.0f;
+// Overflow guard of the softmax weights.  The reference max m is the exact
+// row max of a piece's first 32 keys; later halves use it as long as the
+// weights p = 2^(s*c - m) stay small.  A lane's sum of its 16 weights of a
+// half bounds each of them: while every sum is <= 2^12 no weight exceeds 2^12
+// (ample range for fp32 and bf16); when one is larger (or infinite), that
+// half takes the rare exact path -- its row max, a rescale of O and l, and
+// the weights again.  The result is exact either way after the division by l.
+constexpr float kSumGuard = 4096.0f;
 
 
 // --------------------------------------------------------------------------
@@ -122,8 +127,7 @@ __device__ __forceinline__ int issue_tile(const SrcCursor<D, NW>& c, const LaneC
 template <int D>
 struct WaveState {
   f32x16 o[D / 32];          // O^T accumulators, one per 32-row block of d
-  float m, l;                // running max (base 2) and per-lane partial sum
-  float thr;                 // (m + threshold) / c: raw-score level that moves the max
+  float m, l;                // reference max (base 2) and per-lane partial sum
 };
 
 
@@ -140,28 +144,10 @@ __device__ __forceinline__ float rowmax_half(const f32x16& s) {
   return half_swap_max(fmaxf(a, b));
 }
 
-// Raise the running max when a half's max exceeds it by more than the
-// threshold, rescaling O and the partial sum; run before that half's exps.
-template <int D>
-__device__ __forceinline__ void rescale(float mx, float c, float inv_c, WaveState<D>& st) {
-  if (__builtin_expect(__ballot(mx > st.thr) != 0, 0)) {
-    const float m_new = fmaxf(st.m, mx * c);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
-    st.l *= alpha;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
-    st.m = m_new;
-    st.thr = (m_new + kRescaleTau) * inv_c;
-  }
-}
-
-// P = 2^(s*c - m) as bf16 B operands, and the partial row sum (branch-free;
-// two chains of 8, each starting from its first term).
-template <int D>
-__device__ __forceinline__ void softmax_p(const f32x16& s, float c, WaveState<D>& st, bf16x8 (&pb)[2]) {
-  const float nm = -st.m;
+// P = 2^(s*c - m) as bf16 B operands; returns this lane's sum of the 16
+// weights (two chains of 8, each starting from its first term).
+__device__ __forceinline__ float exp_half(const f32x16& s, float c, float m, bf16x8 (&pb)[2]) {
+  const float nm = -m;
   float lsum[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j)
@@ -171,7 +157,27 @@ __device__ __forceinline__ void softmax_p(const f32x16& s, float c, WaveState<D>
       lsum[j] = e ? lsum[j] + pv : pv;
       pb[j][e] = (__bf16)pv;
     }
-  st.l += lsum[0] + lsum[1];
+  return lsum[0] + lsum[1];
+}
+
+// Softmax weights of one half against the reference max, with the overflow
+// guard: when some lane's sum exceeds kSumGuard (the branch is wave-uniform),
+// raise m to the half's exact row max, rescale O and l, and redo the weights.
+template <int D>
+__device__ __forceinline__ void softmax_p(const f32x16& s, float c, WaveState<D>& st, bf16x8 (&pb)[2]) {
+  float lsum = exp_half(s, c, st.m, pb);
+  if (__builtin_expect(__ballot(lsum > kSumGuard) != 0, 0)) {
+    const float m_new = fmaxf(st.m, rowmax_half(s) * c);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_new);
+    st.l *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st.o[db][r] *= alpha;
+    st.m = m_new;
+    lsum = exp_half(s, c, st.m, pb);
+  }
+  st.l += lsum;
 }
 
 // Pin a value at this program point: the row-sum additions are then issued
@@ -238,7 +244,6 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
   }
 
   const float c = a.scale * kLog2e;
-  const float inv_c = 1.0f / c;
   LaneConst<D, NW> lc;
   lane_const<D, NW>(lc, w, lane);
 
@@ -250,7 +255,6 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[b].o[db][r] = 0.f;
     st[b].m = -INFINITY;
-    st[b].thr = -INFINITY;
     st[b].l = 0.f;
   }
 
@@ -264,23 +268,12 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     if (t >= cur.t1) cursor_set<D, NW>(cur, P.seg, cur.s + 1, h, nh, w, lane);
     return issue_tile<D, NW>(cur, lc, t, lb.k[i], lb.v[i], w);
   };
-  // Scores of a half: keys at or past `limit` masked, then the running max
-  // applied.  The row maxima of the unmasked scores come first, outside the
-  // (rarely taken) masking branch, so that they share a basic block with the
-  // MFMAs issued before them and can overlap them.
-  auto finish_scores = [&](f32x16 (&s)[R], int limit) {
-    float mx[R];
-#pragma unroll
-    for (int b = 0; b < R; ++b) mx[b] = rowmax_half(s[b]);
+  // Scores of a half: keys at or past `limit` masked (a rarely taken branch).
+  auto mask_scores = [&](f32x16 (&s)[R], int limit) {
     if (limit < 32) {
 #pragma unroll
-      for (int b = 0; b < R; ++b) {
-        mask_half(s[b], limit, hl);
-        mx[b] = rowmax_half(s[b]);
-      }
+      for (int b = 0; b < R; ++b) mask_half(s[b], limit, hl);
     }
-#pragma unroll
-    for (int b = 0; b < R; ++b) rescale<D>(mx[b], c, inv_c, st[b]);
   };
   auto softmax = [&](const f32x16 (&s)[R], bf16x8 (&pb)[R][2]) {
 #pragma unroll
@@ -299,12 +292,16 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
   else wait_dma();
   __syncthreads();
   qk_half<D, NW, R>(lb.k[0], 0, lc, qreg, sa);
-  finish_scores(sa, valid[0]);
+  mask_scores(sa, valid[0]);
+  // The reference max: the exact row max of the piece's first half (it holds
+  // at least one unmasked key, so m is finite from here on).
+#pragma unroll
+  for (int b = 0; b < R; ++b) st[b].m = rowmax_half(sa[b]) * c;
 
   // Tile t is in buffer i (landed); buffer i+1 holds tile t+1 and i+2 tile
   // t+2 (both may still be landing); buffer i+3 is free for tile t+3 (indices
   // mod 4).  Copies run two tiles ahead.
-  // Invariant at entry: sa = masked scores of half 0 of tile t, max applied.
+  // Invariant at entry: sa = masked scores of half 0 of tile t.
   auto tile = [&](int t, int i) {
     const int i1 = (i + 1) & 3, i3 = (i + 3) & 3;
     // half 0: S^T(half 1) and softmax(half 0) interleave; then PV(half 0)
@@ -313,7 +310,7 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     pv_half<D, NW, R>(lb.v[i], 0, lc, pb, st);
 #pragma unroll
     for (int b = 0; b < R; ++b) materialize(st[b].l);
-    finish_scores(sb, valid[i] - 32);
+    mask_scores(sb, valid[i] - 32);
     // half 1: S^T(tile t+1, half 0) and softmax(half 1); then PV(half 1).
     // On the last tile the S^T of buffer i+1 is computed on stale data and dropped.
     const bool more = t + 1 < t_end;
@@ -328,7 +325,7 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     pv_half<D, NW, R>(lb.v[i], 1, lc, pb, st);
 #pragma unroll
     for (int b = 0; b < R; ++b) materialize(st[b].l);
-    if (more) finish_scores(sa, valid[i1]);
+    if (more) mask_scores(sa, valid[i1]);
   };
 
   for (int t = t_begin; t < t_end; t += 4) {
