@@ -2,7 +2,9 @@
 
   libff.so            C ABI + gfx950 HIP kernels (hipcc, --offload-arch=gfx950):
                       ff_kernels.hip (renderer / planner attention, bank
-                      copies) and ff_bc_kernels.hip (block-causal backward)
+                      copies), ff_bc_kernels.hip (block-causal backward) and
+                      ff_static_scratch.hip (the fixed device scratch of the
+                      call that allocates nothing)
   libff_hostcheck.so  the same host bookkeeping linked against a recording stub
                       instead of the kernels (g++); CPU tests use it to drive the
                       ABI's success paths without a GPU.
@@ -45,7 +47,7 @@ def build(verbose_resources: bool = False) -> None:
 
     extra = ["-Rpass-analysis=kernel-resource-usage"] if verbose_resources else []
     kern_objs = []
-    for name in ("ff_kernels", "ff_bc_kernels"):
+    for name in ("ff_kernels", "ff_bc_kernels", "ff_static_scratch"):
         src = os.path.join(CSRC, "hip", name + ".hip")
         obj = os.path.join(BUILD, name + ".o")
         _run([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS, *extra, *inc,

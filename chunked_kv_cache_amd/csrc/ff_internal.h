@@ -135,6 +135,14 @@ struct BcLaunch {
 };
 static_assert(sizeof(BcLaunch) <= 4096, "backward launch arguments exceed the kernel argument limit");
 
+// Fixed device scratch of ff_render_attend_static_scratch: the partial slots
+// of one call (two per persistent workgroup, each kBlockM rows of head_dim
+// (<= 128) fp32 values plus the row max and sum), 65 MiB.
+constexpr size_t kStaticScratchBytes = size_t(kMaxWg) * 2 * size_t(kBlockM) * (128 + 2) * 4;
+// Device address and size of that scratch on the current device; the
+// address is taken once per device.  Returns 0, or FF_E_HIP.
+int dev_static_scratch(void** ptr, size_t* bytes);
+
 // Compute units and XCDs of the current device (hipDeviceAttribute*).
 // Returns 0, or FF_E_HIP when the device cannot be queried.
 int dev_topology(int* n_cu, int* n_xcd);

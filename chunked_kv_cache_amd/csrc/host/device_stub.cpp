@@ -47,6 +47,14 @@ int dev_launch_bc_backward(const BcLaunch& b, void*, Profiler*) {
   return 0;
 }
 
+// Host stand-in for the fixed device scratch (never dereferenced by the stub).
+int dev_static_scratch(void** ptr, size_t* bytes) {
+  alignas(256) static uint8_t stand_in[256];
+  *ptr = stand_in;
+  *bytes = kStaticScratchBytes;
+  return 0;
+}
+
 Profiler* dev_profiler_create() { return new Profiler(); }
 void dev_profiler_destroy(Profiler* p) { delete p; }
 void dev_profiler_reset(Profiler*) {}

@@ -347,9 +347,15 @@ ff_status ff_anchor_bank_publish(ff_ctx* c, int first_anchor, int n_anchors, con
   return FF_OK;
 }
 
-ff_status ff_render_attend_grouped(ff_ctx* c, int n_pairs, const int* chunks, const int* stages,
-                                   const void* const* Q, const void* const* K, const void* const* V,
-                                   void* const* O, float* const* lse, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The renderer call(s) of ff_render_attend[_grouped]; `part` (nullable)
+// replaces the workspace's partial region of the call (one pair only).
+ff_status render_attend(ff_ctx* c, int n_pairs, const int* chunks, const int* stages, const void* const* Q,
+                        const void* const* K, const void* const* V, void* const* O, float* const* lse, void* stream,
+                        float* part) {
   if (!c || !chunks || !stages || !Q || !K || !V || !O) return FF_E_INVAL;
   if (n_pairs < 1 || n_pairs > kMaxPairs) return FF_E_INVAL;
   for (int p = 0; p < n_pairs; ++p) {
@@ -388,6 +394,7 @@ ff_status ff_render_attend_grouped(ff_ctx* c, int n_pairs, const int* chunks, co
   // 2) Segmented attention over anchors + history + own (now in the bank).
   AttnLaunch al;
   fill_attention(c, n_pairs, stages, plans, c->Lq, Q, O, lse, &al);
+  if (part) al.pair[0].part = part;
   if (dev_launch_attention(al, stream, prof) != 0) return FF_E_HIP;
 
   for (int p = 0; p < n_pairs; ++p) {
@@ -397,6 +404,16 @@ ff_status ff_render_attend_grouped(ff_ctx* c, int n_pairs, const int* chunks, co
   return FF_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+ff_status ff_render_attend_grouped(ff_ctx* c, int n_pairs, const int* chunks, const int* stages,
+                                   const void* const* Q, const void* const* K, const void* const* V,
+                                   void* const* O, float* const* lse, void* stream) {
+  return render_attend(c, n_pairs, chunks, stages, Q, K, V, O, lse, stream, nullptr);
+}
+
 ff_status ff_render_attend(ff_ctx* c, int chunk, int stage, const void* Q, const void* K, const void* V,
                            void* O, float* lse, void* stream) {
   const void* q[1] = {Q};
@@ -404,7 +421,28 @@ ff_status ff_render_attend(ff_ctx* c, int chunk, int stage, const void* Q, const
   const void* v[1] = {V};
   void* o[1] = {O};
   float* l[1] = {lse};
-  return ff_render_attend_grouped(c, 1, &chunk, &stage, q, k, v, o, l, stream);
+  return render_attend(c, 1, &chunk, &stage, q, k, v, o, l, stream, nullptr);
+}
+
+ff_status ff_render_attend_static_scratch(ff_ctx* c, int chunk, int stage, const void* Q, const void* K,
+                                          const void* V, void* O, float* lse, void* stream) {
+  if (!c) return FF_E_INVAL;
+  // The call's partial slots: two per persistent workgroup.
+  const size_t need = part_region_bytes(c->part_slot_bytes);
+  float* part = nullptr;
+  if (need) {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+    if (dev_static_scratch(&ptr, &bytes) != 0) return FF_E_HIP;
+    if (need > bytes) return FF_E_NOSPACE;
+    part = static_cast<float*>(ptr);
+  }
+  const void* q[1] = {Q};
+  const void* k[1] = {K};
+  const void* v[1] = {V};
+  void* o[1] = {O};
+  float* l[1] = {lse};
+  return render_attend(c, 1, &chunk, &stage, q, k, v, o, l, stream, part);
 }
 
 ff_status ff_plan_attend(ff_ctx* c, int block, const void* Q, const void* K, const void* V, void* O, float* lse,

@@ -69,6 +69,7 @@ _SIGS = {
     "ff_destroy": (None, [_VP]),
     "ff_anchor_bank_publish": (_I, [_VP, _I, _I, _VP, _VP, _VP]),
     "ff_render_attend": (_I, [_VP, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP]),
+    "ff_render_attend_static_scratch": (_I, [_VP, _I, _I, _VP, _VP, _VP, _VP, _VP, _VP]),
     "ff_render_attend_grouped": (_I, [_VP, _I, ctypes.POINTER(_I), ctypes.POINTER(_I), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), ctypes.POINTER(_VP), ctypes.POINTER(_VP),
                                       ctypes.POINTER(_VP), _VP]),
@@ -176,6 +177,12 @@ def ff_render_attend(ctx, chunk, stage, Q, K, V, O, lse=None, stream=None, L=Non
     L = L or lib()
     _check(L.ff_render_attend(ctx, chunk, stage, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
                               _stream(stream, Q)), L)
+
+
+def ff_render_attend_static_scratch(ctx, chunk, stage, Q, K, V, O, lse=None, stream=None, L=None) -> None:
+    L = L or lib()
+    _check(L.ff_render_attend_static_scratch(ctx, chunk, stage, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
+                                             _stream(stream, Q)), L)
 
 
 def ff_render_attend_grouped(ctx, chunks: Sequence[int], stages: Sequence[int], Q, K, V, O, lse=None,

@@ -179,6 +179,24 @@ ff_status ff_render_attend_grouped(ff_ctx* ctx, int n_pairs, const int* chunks, 
                                    const void* const* Q, const void* const* K, const void* const* V,
                                    void* const* O, float* const* lse, void* stream);
 
+/* ff_render_attend_static_scratch -- ff_render_attend for callers that
+ * cannot allocate device memory or have the workspace grow: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, validation, results and bank update as ff_render_attend;
+ * the only difference is where the call's split-item partials live: in a
+ * fixed device array of the library (65 MiB, one per device, held until
+ * the process ends) instead of the workspace's partial region.  The call
+ * itself allocates nothing.  Its first call on a device takes that array's
+ * address (host metadata only).  Every call on one device shares the array
+ * and leaves its contents behind: calls that overlap on one device (other
+ * streams, other contexts, other host threads) race on it and must be
+ * ordered by the caller.  FF_E_NOSPACE if the call's partials would exceed
+ * the array (head_dim <= 128 always fits); FF_E_HIP if its address cannot
+ * be taken.                                                                  */
+ff_status ff_render_attend_static_scratch(ff_ctx* ctx, int chunk, int stage,
+                                          const void* Q, const void* K, const void* V,
+                                          void* O, float* lse, void* stream);
+
 /* ff_bank_tail -- contents of B_k: *n_out chunk ids, oldest first, written to
  * chunk_ids[0..H-1] (host) immediately; if K_out / V_out are non-NULL their
  * bytes ([n*B_R*T][n_heads][head_dim], the published K/V in the same order)
