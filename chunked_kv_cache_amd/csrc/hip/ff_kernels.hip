@@ -618,12 +618,14 @@ __global__ __launch_bounds__(256) void layout_copy_kernel(const CopyLaunch cl) {
 
 // --------------------------------------------------------------------------
 // bf16 publish / unpack with the V transpose done in registers.
-// Block = 128 tokens x 1 head; 4 waves, wave w covers tokens 64*(w/2) .. +63
-// and head-dim 64*(w%2) .. +63.  Lane = tg + 8*c: token group tg (8 tokens),
-// 16-byte d-chunk c.  Each lane moves an 8 x 8 bf16 block: 8 token rows of one
-// d-chunk in, 8 d-rows of one token group out, transposed with byte permutes.
-// For a fixed register, the 64 lanes touch 8 rows x 128 contiguous bytes on
-// both sides.  K moves as plain 16-byte chunks (8 per lane).
+// Block = 256 tokens x 1 head: two groups of 128 tokens; in each group wave w
+// covers tokens 64*(w/2) .. +63 and head-dim 64*(w%2) .. +63.  Lane = tg + 8*c:
+// token group tg (8 tokens), 16-byte d-chunk c.  Each lane moves an 8 x 8
+// bf16 block per group: 8 token rows of one d-chunk in, 8 d-rows of one token
+// group out, transposed with byte permutes.  For a fixed register, the 64
+// lanes touch 8 rows x 128 contiguous bytes on both sides.  K moves as plain
+// 16-byte chunks (8 per lane and group).  The publish issues both groups'
+// loads (32 x 16 bytes per lane) before any store.
 // --------------------------------------------------------------------------
 __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
   // in[j] = 8 bf16 of token j (d = 0..7); out[r] = 8 bf16 of d = r (tokens 0..7)
@@ -636,6 +638,8 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     }
 }
 
+constexpr int kCopyTokens = 256;   // tokens per bf16 copy block
+
 template <bool kPublish>
 __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch cl) {
   constexpr int D = 128;
@@ -645,49 +649,63 @@ __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch 
   if (g >= J.nseg) return;
   const int nh = cl.nh, L = cl.L;
   const int h = blockIdx.x % nh;
-  const int t0 = (blockIdx.x / nh) * 128;
+  const int t0 = (blockIdx.x / nh) * kCopyTokens;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int tg = lane & 7, c = lane >> 3;
-  const int tb = t0 + 64 * (w >> 1) + 8 * tg;        // first token of this lane's group
   const int d0 = 64 * (w & 1) + 8 * c;               // first d of this lane's chunk
-  const bool ok = tb < L;                            // L is a multiple of 8
+  int tb[2];                                         // first token of this lane's group, per 128-token group
+  bool ok[2];                                        // L is a multiple of 8
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    tb[gi] = t0 + 128 * gi + 64 * (w >> 1) + 8 * tg;
+    ok[gi] = tb[gi] < L;
+  }
   uint8_t* blk = static_cast<uint8_t*>(J.block) + int64_t(g) * cl.block_stride;
   __bf16* bk = reinterpret_cast<__bf16*>(blk) + int64_t(h) * L * D;                          // K [h][t][d]
   __bf16* bv = reinterpret_cast<__bf16*>(blk) + int64_t(nh) * L * D + int64_t(h) * D * L;   // V^T [h][d][t]
   const int64_t row0 = int64_t(g) * L;               // first token row of this source
-  u32x4 kin[8], vin[8], vout[8];
   if (kPublish) {
     const __bf16* rk = static_cast<const __bf16*>(J.rows_k);
     const __bf16* rv = static_cast<const __bf16*>(J.rows_v);
-    if (ok) {
+    u32x4 kin[2][8], vin[2][8], vout[8];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      if (!ok[gi]) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int64_t src = ((row0 + tb + j) * nh + h) * D + d0;
-        kin[j] = ld16(rk + src);
-        vin[j] = ld16(rv + src);
+        const int64_t src = ((row0 + tb[gi] + j) * nh + h) * D + d0;
+        kin[gi][j] = ld16(rk + src);
+        vin[gi][j] = ld16(rv + src);
       }
+    }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) st16(bk + int64_t(tb + j) * D + d0, kin[j]);
-      transpose8x8(vin, vout);
+    for (int gi = 0; gi < 2; ++gi) {
+      if (!ok[gi]) continue;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) st16(bv + int64_t(d0 + r) * L + tb, vout[r]);
+      for (int j = 0; j < 8; ++j) st16(bk + int64_t(tb[gi] + j) * D + d0, kin[gi][j]);
+      transpose8x8(vin[gi], vout);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) st16(bv + int64_t(d0 + r) * L + tb[gi], vout[r]);
     }
   } else {
     __bf16* ok_ = static_cast<__bf16*>(J.out_k);
     __bf16* ov_ = static_cast<__bf16*>(J.out_v);
-    if (ok) {
+    u32x4 kin[8], vin[8], vout[8];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      if (!ok[gi]) continue;
       if (ok_) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kin[j] = ld16(bk + int64_t(tb + j) * D + d0);
+        for (int j = 0; j < 8; ++j) kin[j] = ld16(bk + int64_t(tb[gi] + j) * D + d0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) st16(ok_ + ((int64_t(tb) + j) * nh + h) * D + d0, kin[j]);
+        for (int j = 0; j < 8; ++j) st16(ok_ + ((int64_t(tb[gi]) + j) * nh + h) * D + d0, kin[j]);
       }
       if (ov_) {
 #pragma unroll
-        for (int r = 0; r < 8; ++r) vin[r] = ld16(bv + int64_t(d0 + r) * L + tb);
+        for (int r = 0; r < 8; ++r) vin[r] = ld16(bv + int64_t(d0 + r) * L + tb[gi]);
         transpose8x8(vin, vout);       // the 8x8 transpose is its own inverse
 #pragma unroll
-        for (int j = 0; j < 8; ++j) st16(ov_ + ((int64_t(tb) + j) * nh + h) * D + d0, vout[j]);
+        for (int j = 0; j < 8; ++j) st16(ov_ + ((int64_t(tb[gi]) + j) * nh + h) * D + d0, vout[j]);
       }
     }
   }
@@ -755,7 +773,7 @@ int dev_launch_attention(const AttnLaunch& a0, void* stream, Profiler* prof) {
 template <bool kPublish>
 static void launch_copy(const CopyLaunch& c, hipStream_t s) {
   if (c.dtype == FF_BF16 && c.d == 128) {
-    dim3 grid(unsigned(((c.L + 127) / 128) * c.nh), unsigned(c.max_nseg), unsigned(c.n_jobs));
+    dim3 grid(unsigned(((c.L + kCopyTokens - 1) / kCopyTokens) * c.nh), unsigned(c.max_nseg), unsigned(c.n_jobs));
     hipLaunchKernelGGL((layout_copy_bf16_kernel<kPublish>), grid, dim3(256), 0, s, c);
     return;
   }
