@@ -180,11 +180,6 @@ __device__ __forceinline__ void softmax_p(const f32x16& s, float c, WaveState<D>
   st.l += lsum;
 }
 
-// Pin a value at this program point: the row-sum additions are then issued
-// in the same basic block as the MFMAs they can overlap, instead of being
-// sunk past the masking branch that follows.
-__device__ __forceinline__ void materialize(float& x) { asm volatile("" : "+v"(x)); }
-
 // O^T += V^T P^T for one 32-key half of the V^T tile vbuf; each operand read
 // feeds R MFMAs.
 template <int D, int NW, int R>
@@ -308,8 +303,6 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     qk_half<D, NW, R>(lb.k[i], 1, lc, qreg, sb);
     softmax(sa, pb);
     pv_half<D, NW, R>(lb.v[i], 0, lc, pb, st);
-#pragma unroll
-    for (int b = 0; b < R; ++b) materialize(st[b].l);
     mask_scores(sb, valid[i] - 32);
     // half 1: S^T(tile t+1, half 0) and softmax(half 1); then PV(half 1).
     // On the last tile the S^T of buffer i+1 is computed on stale data and dropped.
@@ -323,8 +316,6 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
     qk_half<D, NW, R>(lb.k[i1], 0, lc, qreg, sa);
     softmax(sb, pb);
     pv_half<D, NW, R>(lb.v[i], 1, lc, pb, st);
-#pragma unroll
-    for (int b = 0; b < R; ++b) materialize(st[b].l);
     if (more) mask_scores(sa, valid[i1]);
   };
 
@@ -618,14 +609,16 @@ __global__ __launch_bounds__(256) void layout_copy_kernel(const CopyLaunch cl) {
 
 // --------------------------------------------------------------------------
 // bf16 publish / unpack with the V transpose done in registers.
-// Block = 256 tokens x 1 head: two groups of 128 tokens; in each group wave w
-// covers tokens 64*(w/2) .. +63 and head-dim 64*(w%2) .. +63.  Lane = tg + 8*c:
-// token group tg (8 tokens), 16-byte d-chunk c.  Each lane moves an 8 x 8
+// Block = G x 128 tokens x 1 head: G groups of 128 tokens; in each group wave
+// w covers tokens 64*(w/2) .. +63 and head-dim 64*(w%2) .. +63.  Lane = tg +
+// 8*c: token group tg (8 tokens), 16-byte d-chunk c.  Each lane moves an 8 x 8
 // bf16 block per group: 8 token rows of one d-chunk in, 8 d-rows of one token
 // group out, transposed with byte permutes.  For a fixed register, the 64
 // lanes touch 8 rows x 128 contiguous bytes on both sides.  K moves as plain
-// 16-byte chunks (8 per lane and group).  The publish issues both groups'
-// loads (32 x 16 bytes per lane) before any store.
+// 16-byte chunks (8 per lane and group).  The publish issues all groups'
+// loads (G x 16 x 16 bytes per lane) before any store.  G = 2 when the copy
+// would otherwise take about two rounds of blocks over the CUs (one 480p
+// chunk: 444 blocks of 128 tokens -> 228 of 256), G = 1 for larger copies.
 // --------------------------------------------------------------------------
 __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
   // in[j] = 8 bf16 of token j (d = 0..7); out[r] = 8 bf16 of d = r (tokens 0..7)
@@ -638,9 +631,7 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
     }
 }
 
-constexpr int kCopyTokens = 256;   // tokens per bf16 copy block
-
-template <bool kPublish>
+template <bool kPublish, int G>
 __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch cl) {
   constexpr int D = 128;
   const int job = blockIdx.z, g = blockIdx.y;
@@ -649,14 +640,14 @@ __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch 
   if (g >= J.nseg) return;
   const int nh = cl.nh, L = cl.L;
   const int h = blockIdx.x % nh;
-  const int t0 = (blockIdx.x / nh) * kCopyTokens;
+  const int t0 = (blockIdx.x / nh) * 128 * G;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int tg = lane & 7, c = lane >> 3;
   const int d0 = 64 * (w & 1) + 8 * c;               // first d of this lane's chunk
-  int tb[2];                                         // first token of this lane's group, per 128-token group
-  bool ok[2];                                        // L is a multiple of 8
+  int tb[G];                                         // first token of this lane's group, per 128-token group
+  bool ok[G];                                        // L is a multiple of 8
 #pragma unroll
-  for (int gi = 0; gi < 2; ++gi) {
+  for (int gi = 0; gi < G; ++gi) {
     tb[gi] = t0 + 128 * gi + 64 * (w >> 1) + 8 * tg;
     ok[gi] = tb[gi] < L;
   }
@@ -667,9 +658,9 @@ __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch 
   if (kPublish) {
     const __bf16* rk = static_cast<const __bf16*>(J.rows_k);
     const __bf16* rv = static_cast<const __bf16*>(J.rows_v);
-    u32x4 kin[2][8], vin[2][8], vout[8];
+    u32x4 kin[G][8], vin[G][8], vout[8];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
+    for (int gi = 0; gi < G; ++gi) {
       if (!ok[gi]) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -679,7 +670,7 @@ __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch 
       }
     }
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
+    for (int gi = 0; gi < G; ++gi) {
       if (!ok[gi]) continue;
 #pragma unroll
       for (int j = 0; j < 8; ++j) st16(bk + int64_t(tb[gi] + j) * D + d0, kin[gi][j]);
@@ -692,7 +683,7 @@ __global__ __launch_bounds__(256) void layout_copy_bf16_kernel(const CopyLaunch 
     __bf16* ov_ = static_cast<__bf16*>(J.out_v);
     u32x4 kin[8], vin[8], vout[8];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
+    for (int gi = 0; gi < G; ++gi) {
       if (!ok[gi]) continue;
       if (ok_) {
 #pragma unroll
@@ -773,8 +764,16 @@ int dev_launch_attention(const AttnLaunch& a0, void* stream, Profiler* prof) {
 template <bool kPublish>
 static void launch_copy(const CopyLaunch& c, hipStream_t s) {
   if (c.dtype == FF_BF16 && c.d == 128) {
-    dim3 grid(unsigned(((c.L + kCopyTokens - 1) / kCopyTokens) * c.nh), unsigned(c.max_nseg), unsigned(c.n_jobs));
-    hipLaunchKernelGGL((layout_copy_bf16_kernel<kPublish>), grid, dim3(256), 0, s, c);
+    int n_cu = 0, n_xcd = 0;
+    if (dev_topology(&n_cu, &n_xcd) != 0) n_cu = kMaxWg;
+    const int64_t blocks128 = int64_t((c.L + 127) / 128) * c.nh * c.max_nseg * c.n_jobs;
+    if (blocks128 <= 2 * int64_t(n_cu)) {
+      dim3 grid(unsigned(((c.L + 255) / 256) * c.nh), unsigned(c.max_nseg), unsigned(c.n_jobs));
+      hipLaunchKernelGGL((layout_copy_bf16_kernel<kPublish, 2>), grid, dim3(256), 0, s, c);
+    } else {
+      dim3 grid(unsigned(((c.L + 127) / 128) * c.nh), unsigned(c.max_nseg), unsigned(c.n_jobs));
+      hipLaunchKernelGGL((layout_copy_bf16_kernel<kPublish, 1>), grid, dim3(256), 0, s, c);
+    }
     return;
   }
   dim3 grid(unsigned(((c.L + 63) / 64) * c.nh), unsigned(c.max_nseg), unsigned(c.n_jobs));

@@ -152,6 +152,7 @@ class Pair:
             for (i, k), d, o, l in zip(pairs, dev, outs, lses):
                 ff.ff_render_attend(self.ctx, i, k, d[0], d[1], d[2], o, l)
         torch.cuda.synchronize()
+        self.last_outs = list(zip(outs, lses))          # the whole outputs of the last step, on the device
         results = []
         for j, ((i, k), h) in enumerate(zip(pairs, host)):
             q64, k64, v64 = (syn.as_f64(x, c.dtype) for x in h)
