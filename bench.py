@@ -8,7 +8,9 @@ included.  The default workload is the 480p-shaped step: 12 heads, head_dim
 chunks + own = 20 latents: 4680 queries x 31200 keys).  Steps rotate over the
 S = 4 stage banks (4 distinct key sets, 0.77 GB, more than the 256 MB
 last-level cache); before each round the four banks are rewound by one chunk
-(ff_stage_bank_rewind) so the same steady-state call repeats.
+(ff_stage_bank_rewind) so the same steady-state call repeats, with the
+in-flight Q/K/V alternating between two input sets per stage from round to
+round (8 distinct publish sources).
 
 `--workload plan480` measures the planner role instead: one step is one
 denoising ff_plan_attend call of planner block 8 of a 261-latent clip
@@ -155,11 +157,20 @@ def main():
         for k in reversed(range(S)):
             ff.ff_stage_bank_rewind(ctx, k)
 
+    # A second input set per stage (seeded N(0,1) bf16 drawn on the device): the
+    # rounds alternate between the two, so the publishes read 8 distinct
+    # 28.75 MB source sets in turn (and each publish follows an attention that
+    # streamed a 192 MB key set), which keeps the sources out of the 256 MB
+    # last-level cache.
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    randn = lambda: torch.randn((Lq, nh, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    alt_inputs = {k: (randn(), randn(), randn()) for k in range(S)}
+
     def one_step(j):
         k = j % S
         if k == 0:
             rewind_all()
-        qd, kd, vd = step_inputs[k][:3]
+        qd, kd, vd = (step_inputs[k][:3] if (j // S) % 2 == 0 else alt_inputs[k])
         ff.ff_render_attend(ctx, chunk, k, qd, kd, vd, outs[k], lses[k], stream=stream)
 
     # the stage banks currently hold chunk `chunk` published once; start a round

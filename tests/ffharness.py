@@ -35,6 +35,45 @@ def wavefront(case: "Case"):
     return [ff.ff_wavefront(shape, case.S, t) for t in range(n)]
 
 
+def whole_head_reference(pr: "Pair", i: int, k: int, heads):
+    """Oracle O and LSE of call (i, k) on every query row of the given heads,
+    from the oracle's state before the call (one head's keys at a time, so
+    full-size calls stay cheap).  Returns {head: (O [Lq, 1, d], LSE [1, Lq])}."""
+    c = pr.case
+    bank = {cid: (Kb, Vb) for cid, Kb, Vb in pr.ro.banks[k]}
+    q, kk, vv = pr.gen(i, k)
+    out = {}
+    for hh in heads:
+        one = lambda x: syn.as_f64(x[:, hh:hh + 1], c.dtype)
+        ks, vs = [], []
+        for kind, idx in pr.ro.key_sources(i, k):
+            if kind == "own":
+                ks.append(one(kk))
+                vs.append(one(vv))
+            else:
+                Ks, Vs = pr.ro.anchors[idx] if kind == "anchor" else bank[idx]
+                ks.append(Ks[:, hh:hh + 1])
+                vs.append(Vs[:, hh:hh + 1])
+        out[hh] = orc.attention(one(q), np.concatenate(ks), np.concatenate(vs), pr.cfg.scale)
+    return out
+
+
+def check_whole_heads(pr: "Pair", refs) -> list:
+    """Compare the last step's device output with whole_head_reference(); returns
+    (head, max |dO|, relative Frobenius) per head."""
+    res = []
+    dt = pr.case.dtype
+    for hh, (O_ref, L_ref) in refs.items():
+        o, l = pr.last_outs[0]
+        O = from_device_f64(o[:, hh:hh + 1])
+        L = l[hh:hh + 1].cpu().numpy().astype(np.float64)
+        err = np.abs(O - O_ref).max()
+        relf = np.linalg.norm(O - O_ref) / np.linalg.norm(O_ref)
+        assert err <= TOL[dt] and relf <= RELF_TOL[dt] and np.abs(L - L_ref).max() <= LSE_TOL[dt], (hh, err, relf)
+        res.append((hh, err, relf))
+    return res
+
+
 def to_device(x: np.ndarray, dtype: str):
     import torch
     if dtype == "bf16":

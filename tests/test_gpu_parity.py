@@ -196,14 +196,19 @@ def test_planner_480p_block_sampled_rows():
 def test_480p_steps_sampled_rows():
     """480p shape (T=1560, 12 heads, d=128) at stage 0, chunks 0..13: chunk 5 is the
     first 20-latent step (31200 keys), chunk 13 the 21-latent one (32760 keys, three
-    anchors).  Outputs on 64 sampled query rows per call, banks bit-exact."""
+    anchors).  Outputs on 64 sampled query rows per call, banks bit-exact;
+    chunks 5 and 13 also whole (all 4680 rows) on heads 0 and 11."""
+    from ffharness import check_whole_heads, whole_head_reference
     case = Case(T=1560, nh=12, d=128, S=1)
     rows = np.sort(np.random.default_rng(7).choice(3 * 1560, size=64, replace=False))
     pr = Pair(case)
     try:
         pr.publish_anchors()
         for i in range(14):
+            whole = whole_head_reference(pr, i, 0, (0, 11)) if i in (5, 13) else {}
             pr.step([(i, 0)], grouped=False, rows=rows, control=i in (5, 13))
+            for hh, err, relf in check_whole_heads(pr, whole):
+                print(f"480p chunk {i} head {hh}, all rows: max|dO|={err:.2e} relF={relf:.2e}")
         print(f"480p chunks 0..13: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
               f"control>={pr.stats.min_control_ratio:.1f}x")
     finally:
@@ -241,37 +246,16 @@ def test_720p_step_sampled_rows():
     against the oracle over that head's 75600 keys."""
     import sys
 
-    import synthetic as syn
-    from ffharness import LSE_TOL, RELF_TOL, TOL
+    from ffharness import check_whole_heads, whole_head_reference
     case = Case(T=3600, nh=40, d=128, S=1)
     rows = np.sort(np.random.default_rng(5).choice(3 * 3600, size=8, replace=False))
     pr = Pair(case, device_bank_check=True)
     try:
         pr.publish_anchors()
         for i in range(14):
-            whole = {}
-            if i == 13:
-                # the oracle's key set of the call, per checked head, gathered before the call
-                bank = {cid: (Kb, Vb) for cid, Kb, Vb in pr.ro.banks[0]}
-                q, kk, vv = pr.gen(13, 0)
-                for hh in (0, 39):
-                    ks, vs = [], []
-                    for kind, idx in pr.ro.key_sources(13, 0):
-                        Ks, Vs = (pr.ro.anchors[idx] if kind == "anchor" else bank[idx] if kind == "history"
-                                  else (syn.as_f64(kk[:, hh:hh + 1], "bf16"), syn.as_f64(vv[:, hh:hh + 1], "bf16")))
-                        ks.append(Ks[:, hh:hh + 1] if Ks.shape[1] > 1 else Ks)
-                        vs.append(Vs[:, hh:hh + 1] if Vs.shape[1] > 1 else Vs)
-                    whole[hh] = orc.attention(syn.as_f64(q[:, hh:hh + 1], "bf16"), np.concatenate(ks),
-                                              np.concatenate(vs), case.cfg.scale)
+            whole = whole_head_reference(pr, 13, 0, (0, 39)) if i == 13 else {}
             pr.step([(i, 0)], grouped=False, rows=rows, control=i in (5, 13))
-            for hh, (O_ref, L_ref) in whole.items():
-                o, l = pr.last_outs[0]
-                O = o[:, hh:hh + 1].float().cpu().numpy().astype(np.float64)
-                L = l[hh:hh + 1].cpu().numpy().astype(np.float64)
-                err = np.abs(O - O_ref).max()
-                relf = np.linalg.norm(O - O_ref) / np.linalg.norm(O_ref)
-                assert err <= TOL["bf16"] and relf <= RELF_TOL["bf16"] and np.abs(L - L_ref).max() <= LSE_TOL["bf16"], \
-                    (hh, err, relf)
+            for hh, err, relf in check_whole_heads(pr, whole):
                 print(f"  720p chunk 13 head {hh}, all rows: max|dO|={err:.2e} relF={relf:.2e}", flush=True,
                       file=sys.stderr)
             print(f"  720p chunk {i} ok", flush=True, file=sys.stderr)
