@@ -247,8 +247,9 @@ ff_status ff_planner_block(const ff_shape* shape, int block, int* first_anchor, 
  * abstract: once chunk i finishes stage k, its stage-k cache is ready for
  * chunk i+1.  Every dependency of a call on diagonal t -- (i-1, k) and
  * (i, k-1) -- lies on diagonal t-1, so the calls of one diagonal are
- * independent (one per stage: one ff_render_attend_grouped launch), and
- * t = 0 .. N_c+n_stages-2 in order runs every call of the clip legally.
+ * independent (one per stage: one ff_render_attend_grouped launch, or
+ * several when a diagonal holds more than its 8 pairs -- any split is legal),
+ * and t = 0 .. N_c+n_stages-2 in order runs every call of the clip legally.
  * Host only; FF_E_RANGE for t outside that range.                          */
 ff_status ff_wavefront(const ff_shape* shape, int n_stages, int t, int* n_pairs, int* chunks, int* stages);
 

@@ -479,3 +479,124 @@ def test_partial_regions_are_per_stage():
             assert [f(p, hc.ws) for p in range(m)] == [part_off + k * region for _, k in diag]
     finally:
         hc.close()
+
+
+# --------------------------------------------------------------------------
+# Random call sequences: the library accepts exactly the calls the oracle's
+# contract accepts, and the banks then hold the same chunk ids
+# --------------------------------------------------------------------------
+from hypothesis import HealthCheck, given, settings, strategies as st
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(st.lists(st.tuples(st.sampled_from(["render", "next", "next", "next", "anchors"]), st.integers(0, 28),
+                          st.integers(0, 3)), min_size=1, max_size=120),
+       st.sampled_from([orc.GAMMA_BRACKET, orc.GAMMA_CENTER_LR]))
+def test_random_call_sequences_match_the_oracle_contract(ops, rule):
+    cfg = orc.FFConfig(tokens_per_latent=8, n_heads=1, head_dim=64, n_stages=3, history=2, gamma_rule=rule)
+    hc = HostCtx(cfg)
+    ro = orc.Rollout(cfg)
+    blocks = orc.planner_blocks(cfg)
+    z = np.zeros((24, 1, 64))
+    try:
+        for op, a, b in ops:
+            if op == "anchors":
+                blk = blocks[a % len(blocks)]
+                lib_ok = orc_ok = True
+                try:
+                    ff.ff_anchor_bank_publish(hc.ctx, blk[0], len(blk), FAKE, FAKE, L=hc.L)
+                except ff.FFError as e:
+                    lib_ok = False
+                    assert e.status == ff.FF_E_ANCHOR_EXISTS
+                try:
+                    ro.publish_anchors(blk[0], np.zeros((8 * len(blk), 1, 64)), np.zeros((8 * len(blk), 1, 64)))
+                except orc.ContractError:
+                    orc_ok = False
+                assert lib_ok == orc_ok
+                continue
+            # "render": any chunk (27, 28 and stage 3 are out of range); "next": the
+            # chunk the stage expects, which may still lack its anchors or stage k-1
+            k = b
+            i = ro.next_chunk[k] if op == "next" and k < cfg.n_stages else a
+            lib_ok = orc_ok = True
+            try:
+                ff.ff_render_attend(hc.ctx, i, k, FAKE, FAKE, FAKE, FAKE, L=hc.L)
+            except ff.FFError as e:
+                lib_ok = False
+                assert e.status in (ff.FF_E_ORDER, ff.FF_E_ANCHOR_MISSING, ff.FF_E_RANGE)
+            try:
+                ro.render_attend(i, k, None, z, z, compute=False)
+            except orc.ContractError:
+                orc_ok = False
+            assert lib_ok == orc_ok, (op, i, k)
+            if lib_ok:
+                assert ff.ff_bank_tail(hc.ctx, k, L=hc.L) == ro.bank_tail(k)[0]
+        for k in range(cfg.n_stages):
+            assert ff.ff_bank_tail(hc.ctx, k, L=hc.L) == ro.bank_tail(k)[0]
+            assert ff.ff_stage_next(hc.ctx, k, L=hc.L) == ro.next_chunk[k]
+    finally:
+        hc.close()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_walks_through_whole_clips(seed):
+    """Seeded random walks that mostly attempt each stage's next chunk (with
+    anchor blocks published in random order along the way) run deep into the
+    clip; at every step the library and the oracle accept the same calls, and
+    rewinds are checked against the oracle state before the undone call."""
+    import copy
+    rng = np.random.default_rng(seed)
+    cfg = orc.FFConfig(tokens_per_latent=8, n_heads=1, head_dim=64, n_stages=3, history=2,
+                       gamma_rule=[orc.GAMMA_BRACKET, orc.GAMMA_CENTER_LR][seed % 2])
+    hc = HostCtx(cfg)
+    ro = orc.Rollout(cfg)
+    undo = {}
+    blocks = orc.planner_blocks(cfg)
+    order = list(rng.permutation(len(blocks)))
+    z = np.zeros((24, 1, 64))
+    accepted = 0
+    try:
+        for _ in range(400):
+            r = rng.random()
+            if r < 0.05 and order:
+                blk = blocks[order.pop()]
+                ff.ff_anchor_bank_publish(hc.ctx, blk[0], len(blk), FAKE, FAKE, L=hc.L)
+                ro.publish_anchors(blk[0], np.zeros((8 * len(blk), 1, 64)), np.zeros((8 * len(blk), 1, 64)))
+                continue
+            k = int(rng.integers(0, 3))
+            if r < 0.10:                                      # rewind stage k
+                try:
+                    ff.ff_stage_bank_rewind(hc.ctx, k, L=hc.L)
+                    lib_ok = True
+                except ff.FFError as e:
+                    lib_ok = False
+                    assert e.status == ff.FF_E_STATE
+                # the oracle side: allowed once per call, only if stage k+1 has not consumed it
+                orc_ok = k in undo and not (k + 1 < cfg.n_stages and ro.next_chunk[k + 1] > ro.next_chunk[k] - 1)
+                assert lib_ok == orc_ok
+                if orc_ok:                                    # stage k back to before its last call
+                    snap = undo.pop(k)
+                    ro.banks[k] = snap.banks[k]
+                    ro.next_chunk[k] = snap.next_chunk[k]
+                continue
+            i = ro.next_chunk[k] if r < 0.9 else int(rng.integers(0, 27))
+            before = copy.deepcopy(ro)
+            try:
+                ff.ff_render_attend(hc.ctx, i, k, FAKE, FAKE, FAKE, FAKE, L=hc.L)
+                lib_ok = True
+            except ff.FFError:
+                lib_ok = False
+            try:
+                ro.render_attend(i, k, None, z, z, compute=False)
+                orc_ok = True
+            except orc.ContractError:
+                orc_ok = False
+            assert lib_ok == orc_ok, (i, k)
+            if orc_ok:
+                accepted += 1
+                undo[k] = before
+            for kk in range(cfg.n_stages):
+                assert ff.ff_bank_tail(hc.ctx, kk, L=hc.L) == ro.bank_tail(kk)[0]
+        assert accepted >= 40
+    finally:
+        hc.close()
