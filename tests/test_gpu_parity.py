@@ -344,6 +344,76 @@ def test_two_streams_one_stage_each():
         pr.close()
 
 
+def test_graph_capture_rollout():
+    """A whole grouped rollout captured into one HIP graph and replayed three
+    times, with eager work and synchronizations between the replays.  The
+    renderer calls enqueue kernel launches only (no allocation, memset, copy
+    or host wait), so a replay recomputes the rollout from the anchors: every
+    replay's outputs, and the stage banks after it, equal the eager rollout's
+    bit for bit (items are cut, so the merge kernel is in the graph too)."""
+    import torch
+
+    from chunked_kv_cache_amd import ff
+    from ffharness import to_device
+    case = Case(T=48, nh=2, d=128, S=2, n_latents=21)
+    diags = wavefront(case)
+
+    def setup():
+        pr = Pair(case, oracle_compute=False)
+        pr.publish_anchors()
+        ins = {p: [to_device(x, "bf16") for x in pr.gen(*p)] for d in diags for p in d}
+        outs = {p: (torch.empty_like(ins[p][0]), torch.empty((case.nh, 3 * case.T), dtype=torch.float32,
+                                                               device="cuda")) for p in ins}
+        torch.cuda.synchronize()
+        return pr, ins, outs
+
+    def rollout(pr, ins, outs):
+        for d in diags:
+            ff.ff_render_attend_grouped(pr.ctx, [i for i, _ in d], [k for _, k in d], [ins[p][0] for p in d],
+                                        [ins[p][1] for p in d], [ins[p][2] for p in d],
+                                        [outs[p][0] for p in d], [outs[p][1] for p in d])
+
+    def banks(pr):
+        res = []
+        for k in range(case.S):
+            Ko = torch.empty((case.H * 3 * case.T, case.nh, case.d), dtype=torch.bfloat16, device="cuda")
+            Vo = torch.empty_like(Ko)
+            ids = ff.ff_bank_tail(pr.ctx, k, Ko, Vo)
+            torch.cuda.synchronize()
+            res.append((ids, Ko.view(torch.int16).cpu().numpy(), Vo.view(torch.int16).cpu().numpy()))
+        return res
+
+    eager, e_ins, e_outs = setup()
+    graph, g_ins, g_outs = setup()
+    try:
+        rollout(eager, e_ins, e_outs)
+        torch.cuda.synchronize()
+        ref = {p: (o.view(torch.int16).cpu().numpy(), l.cpu().numpy()) for p, (o, l) in e_outs.items()}
+        ref_banks = banks(eager)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            rollout(graph, g_ins, g_outs)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for o, l in g_outs.values():
+                o.fill_(float("nan"))
+                l.fill_(float("nan"))
+            noise = torch.randn(1 << 20, device="cuda").sum()          # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.isfinite(noise)
+            for p, (o, l) in g_outs.items():
+                assert np.array_equal(o.view(torch.int16).cpu().numpy(), ref[p][0]), (rep, p)
+                assert np.array_equal(l.cpu().numpy(), ref[p][1]), (rep, p)
+            for (ids, Kb, Vb), (rids, rK, rV) in zip(banks(graph), ref_banks):
+                assert ids == rids and np.array_equal(Kb, rK) and np.array_equal(Vb, rV), rep
+        del g
+    finally:
+        eager.close()
+        graph.close()
+
+
 def test_65s_rollout_grouped_full_size():
     """The 65 s rollout at its stated shape: 480p (T = 1560, 12 heads, d = 128),
     261 latents, 27 anchors in 9 planner blocks, 87 chunks x 4 stages = 348
