@@ -41,6 +41,10 @@
  *    failed after validation: host metadata is left unchanged, device bank
  *    bytes of the slot being written are undefined.
  *  - One context is used by one host thread at a time (no internal locking).
+ *  - The calls enqueue kernel launches only (no allocation, memset, copy or
+ *    host wait), so they may be captured into a HIP graph.  A replay repeats
+ *    the captured device work; the host bookkeeping (ring slots, next chunk
+ *    of each stage) advanced once, at capture.
  */
 #ifndef FF_H_
 #define FF_H_
