@@ -3,7 +3,8 @@
 //  attn_bf16<D>   segmented flash attention: bf16 MFMA 32x32x16 for S^T = K Q^T
 //                 and O^T = V^T P^T, fp32 online softmax in base 2, K/V tiles
 //                 gathered from the anchor bank and the stage ring through the
-//                 call's key-source table into LDS (no concatenation copy).
+//                 call's key-source table into LDS (no concatenation copy);
+//                 64 query rows per wave at head dim 128, 32 at head dim 64.
 //  attn_f32<D>    plain fp32 path (one lane per query row and head).
 //  merge_pieces   LSE merge of the items cut in the last scheduling round.
 //  publish        token-major K/V -> bank block (K head-major, V transposed).
@@ -57,11 +58,11 @@ constexpr float kSumGuard = 4096.0f;
 // conflict-free 16-byte reads; the swizzle is applied by choosing which
 // global chunk each lane fetches.
 // --------------------------------------------------------------------------
-// Waves per work item.  Wave w owns 256 / NW query rows as blocks of 32; every
-// K or V^T operand read from LDS feeds one MFMA per block.  Eight waves (two
-// per SIMD, 32 rows each) let one wave's LDS reads and softmax hide behind
-// the other's MFMAs; four waves of 64 rows halve the LDS reads but leave each
-// SIMD a single instruction stream, and measure slower.
+// Waves per work item: eight, two per SIMD.  Head dim 128 runs the 64-row
+// form (run_item_w64: waves w and w+4 share 64 query rows and split every
+// tile's keys, each K or V^T operand read feeds two MFMAs); head dim 64 runs
+// the 32-row form (run_item: wave w owns rows 32w..32w+31, one MFMA per
+// operand read, the S^T of the next half beside the softmax of this one).
 constexpr int kAttnWaves = 8;
 
 
@@ -158,6 +159,32 @@ __device__ __forceinline__ float exp_half(const f32x16& s, float c, float m, bf1
       pb[j][e] = (__bf16)pv;
     }
   return lsum[0] + lsum[1];
+}
+
+// The weights of a half in place: the bf16 pair of registers 8j+2e, 8j+2e+1
+// goes to register 8j+e (e < 4), so registers 8j..8j+3 end as the B operand
+// of the PV MFMA for keys 16j..16j+15.  Returns this lane's sum of the 16
+// weights (fp32, before rounding).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float exp_inplace(f32x16& s, float c, float m) {
+  const float nm = -m;
+  float lsum[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[8 * j + 2 * e], c, nm));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[8 * j + 2 * e + 1], c, nm));
+      lsum[j] = (e ? lsum[j] + p0 : p0) + p1;
+      const bf16x2 pk = {(__bf16)p0, (__bf16)p1};
+      s[8 * j + e] = __builtin_bit_cast(float, pk);
+    }
+  return lsum[0] + lsum[1];
+}
+__device__ __forceinline__ bf16x8 p_operand(const f32x16& s, int j) {
+  const f32x16 t = s;
+  return j ? __builtin_bit_cast(bf16x8, __builtin_shufflevector(t, t, 8, 9, 10, 11))
+           : __builtin_bit_cast(bf16x8, __builtin_shufflevector(t, t, 0, 1, 2, 3));
 }
 
 // Softmax weights of one half against the reference max, with the overflow
@@ -367,6 +394,361 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
   }
 }
 
+// --------------------------------------------------------------------------
+// 64 query rows per wave (head_dim 128).
+//
+// Every K or V^T operand read from LDS feeds two MFMAs (two blocks of 32
+// query rows): half the LDS read traffic per MFMA of the 32-row form, whose
+// operand reads alone would take the whole LDS read bandwidth (128 bytes per
+// clock per CU) at the matrix pipes' full rate.  The registers of 64 rows
+// (O^T 128, Q 64, scores 32, weights 16) leave no room for a second score
+// buffer, so a wave runs S^T, softmax and PV of its part of a tile in
+// sequence, and the two waves of each SIMD (w and w+4) interleave instead.
+// They hold the same 64 query rows: wave w < 4 takes keys 0..31 of every
+// 64-key tile, wave w+4 keys 32..63.  The one workgroup barrier per tile is
+// reached by the first group after its softmax and by the second before it,
+// which keeps one wave of each SIMD in its VALU phase while the other runs
+// its MFMAs (PV of this tile, then S^T of the next).  At the end the two
+// partial (m, l, O) of each row are merged through LDS.
+// --------------------------------------------------------------------------
+
+// S^T of one key half for the wave's two row blocks.  kread is the lane's
+// offset for k-step 0 of that half; with the D = 128 swizzle, k-step ks sits
+// at kread ^ (ks << 5) (the swizzle XORs the chunk index, and ks occupies its
+// bits 1..3).
+__device__ __forceinline__ void qk_w64(const uint8_t* kbuf, uint32_t kread, const bf16x8 (&qreg)[2][8],
+                                       f32x16 (&s)[2]) {
+  const f32x16 zero = {};
+  s[0] = zero;
+  s[1] = zero;
+  // Each operand read is issued one k-step ahead of its two MFMAs; the
+  // scheduling barriers keep that order (left alone, the scheduler waits on
+  // every read before its MFMAs).
+  bf16x8 cur = __builtin_bit_cast(bf16x8, ld16(kbuf + kread));
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    bf16x8 nxt = cur;
+    if (ks < 7) nxt = __builtin_bit_cast(bf16x8, ld16(kbuf + (kread ^ uint32_t((ks + 1) << 5))));
+    __builtin_amdgcn_sched_barrier(0);
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qreg[0][ks], s[0], 0, 0, 0);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qreg[1][ks], s[1], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+  }
+}
+
+// O^T += V^T P^T over one key half; vread[j] is the lane's (biased) offset of
+// the half's V^T operand j, rows 0..31.  Reads one step ahead, as above.
+__device__ __forceinline__ void pv_w64(const uint8_t* vbuf, const uint32_t (&vread)[2], const f32x16 (&sp)[2],
+                                       WaveState<128> (&st)[2]) {
+  auto rd = [&](int k) {
+    const int j = k >> 2, db = k & 3;
+    return __builtin_bit_cast(
+        bf16x8, ld16(vbuf + (int32_t(vread[j]) - int32_t(kLdsBias)) + db * 32 * kBlockN * 2));
+  };
+  bf16x8 cur = rd(0);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int j = k >> 2, db = k & 3;
+    bf16x8 nxt = cur;
+    if (k < 7) nxt = rd(k + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    st[0].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, j ? p_operand(sp[0], 1) : p_operand(sp[0], 0),
+                                                          st[0].o[db], 0, 0, 0);
+    st[1].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, j ? p_operand(sp[1], 1) : p_operand(sp[1], 0),
+                                                          st[1].o[db], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+  }
+}
+
+// Lower bound of a wave's reference max.  The second group's first half may
+// hold no valid key (a piece whose first tile has at most 32); its weights
+// against this bound overflow to infinity on the first valid key, which takes
+// the exact path of the softmax (rescale factor 0 on the empty O and l).
+constexpr float kMaxFloor = -1.0e30f;
+
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// The lane's index, read afresh (volatile, so never merged with an earlier
+// read): lane-derived offsets are recomputed where they are needed instead of
+// holding registers across the key loop.
+__device__ __forceinline__ int lane_now() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return int(l);
+}
+
+// Operand offsets of one wave's key half (hk) for lane `lane`: K operand of
+// k-step 0 (k-step ks at ^ (ks << 5)), V^T operands j = 0, 1 (+ kLdsBias).
+struct HalfOffsets {
+  uint32_t k, v0, v1;
+};
+__device__ __forceinline__ HalfOffsets half_offsets(int lane, int hk) {
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
+  HalfOffsets o;
+  o.k = uint32_t(hk * 32 * 128 * 2 + prow * 128 * 2 + ((hl ^ krow_swz<128>(prow)) << 4));
+  const uint32_t v = uint32_t(l32 * kBlockN * 2 + (((4 * hk + hl) ^ vrow_swz(l32)) << 4)) + kLdsBias;
+  o.v0 = opaque(v);
+  o.v1 = opaque(v ^ 32u);
+  return o;
+}
+
+template <int D>
+__device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaunch& P, int item, int t_begin,
+                                             int t_end, float* slot, const LdsBufs& lb) {
+  static_assert(D == 128, "the 64-row form is laid out for head_dim 128");
+  constexpr int NW = 8;
+  constexpr int KS = D / 16;
+  constexpr int kDma = TileCfg<D, NW>::kDmaPerTile;   // per wave
+  static_assert(TileCfg<D, NW>::kKBlocks == 2 && TileCfg<D, NW>::kVBlocks == 2, "two copies of each per wave");
+  const int nh = a.nh, lq = a.lq;
+  const int qt = item % a.n_qtiles;
+  const int h = item / a.n_qtiles;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hk = w >> 2;                         // key half of every tile
+
+  // Register block b holds rows 64 * (w & 3) + 32 * (b ^ hk) + lane % 32:
+  // each wave keeps block 0 to the end and hands block 1 to its partner, whose
+  // block 0 they are.
+  bf16x8 qreg[2][KS];
+  {
+    const int lane = lane_now();
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int q = qt * kBlockM + (w & 3) * 64 + 32 * (b ^ hk) + (lane & 31);
+      const bool ok = q < lq;
+      const __bf16* qp = static_cast<const __bf16*>(P.q) + (int64_t(ok ? q : 0) * nh + h) * D + 8 * (lane >> 5);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = ld16(qp + 16 * ks);
+        if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+        qreg[b][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  }
+
+  const float c = a.scale * kLog2e;
+  WaveState<D> st[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) st[b].o[db][r] = 0.f;
+    st[b].l = 0.f;
+  }
+
+  // The lane offsets of the tile copies are used once per tile: they wait in
+  // LDS (each lane reads back only what it wrote), not in registers.
+  __shared__ u32x2 kdo[NW * 64], vdo[NW * 64];
+  {
+    const int lane = lane_now();
+    LaneConst<D, NW> lc;
+    lane_const<D, NW>(lc, w, lane);
+    kdo[w * 64 + lane] = u32x2{lc.kdma[0], lc.kdma[1]};
+  }
+  SrcCursor<D, NW> cur;
+  auto set_cursor = [&](int s) {
+    const int lane = lane_now();
+    cursor_set<D, NW>(cur, P.seg, s, h, nh, w, lane);
+    vdo[w * 64 + lane] = u32x2{cur.vdma[0], cur.vdma[1]};
+  };
+  {
+    int s = 0;
+    while (s + 1 < P.seg.nseg && t_begin >= P.seg.tile_start[s + 1]) ++s;
+    set_cursor(s);
+  }
+  auto issue = [&](int t, int i) -> int {
+    if (t >= cur.t1) set_cursor(cur.s + 1);
+    const int lane = lane_now();
+    const int o = (t - cur.t0) * kBlockN;
+    const u32x2 ko = kdo[w * 64 + lane], vo = vdo[w * 64 + lane];
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(cur.k + int64_t(o) * D, uint32_t(cur.n - o) * D * 2);
+    dma16(rk, ko[0], lb.k[i] + (w * 2) * 1024);
+    dma16(rk, ko[1], lb.k[i] + (w * 2 + 1) * 1024);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(cur.v + o, uint32_t(D * cur.n - o) * 2);
+    dma16(rv, vo[0], lb.v[i] + (w * 2) * 1024);
+    dma16(rv, vo[1], lb.v[i] + (w * 2 + 1) * 1024);
+    return min(kBlockN, cur.n - o);
+  };
+  // S^T of this wave's half of the tile in kbuf, keys at or past `valid`
+  // masked (a rarely taken branch).
+  const HalfOffsets ho = half_offsets(lane_now(), hk);
+  auto scores = [&](const uint8_t* kbuf, int valid, f32x16 (&s)[2]) {
+    qk_w64(kbuf, ho.k, qreg, s);
+    const int limit = valid - 32 * hk;
+    if (limit < 32) {
+      const int hl = lane_now() >> 5;
+      mask_half(s[0], limit, hl);
+      mask_half(s[1], limit, hl);
+    }
+  };
+
+  f32x16 sa[2];
+  int valid[4];
+  __syncthreads();       // the previous piece's reads of the buffers are done
+  valid[0] = issue(t_begin, 0);
+  if (t_begin + 1 < t_end) valid[1] = issue(t_begin + 1, 1);
+  if (t_begin + 2 < t_end) valid[2] = issue(t_begin + 2, 2);
+  if (t_begin + 2 < t_end) wait_dma_but<2 * kDma>();
+  else if (t_begin + 1 < t_end) wait_dma_but<kDma>();
+  else wait_dma();
+  wg_barrier();
+  scores(lb.k[0], valid[0], sa);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) st[b].m = fmaxf(rowmax_half(sa[b]) * c, kMaxFloor);
+
+  // Tile t is in buffer i (landed); i+1 holds tile t+1 and i+2 tile t+2 (both
+  // may still be landing); i+3 is free for tile t+3 once every wave is past
+  // this tile's barrier (indices mod 4).  Every wave passes one barrier per
+  // tile.  Invariant at entry: sa = masked scores of this wave's half of tile t.
+  auto tile = [&](int t, int i) {
+    const int i1 = (i + 1) & 3, i3 = (i + 3) & 3;
+    const bool more = t + 1 < t_end;
+    auto sync = [&] {
+      if (more && t + 2 < t_end) wait_dma_but<kDma>();   // tile t+1 landed, t+2 may fly
+      else wait_dma();
+      wg_barrier();
+    };
+    if (hk) sync();
+    {
+      float ls0 = exp_inplace(sa[0], c, st[0].m), ls1 = exp_inplace(sa[1], c, st[1].m);
+      if (__builtin_expect(__ballot(ls0 > kSumGuard || ls1 > kSumGuard) != 0, 0)) {
+        // Rare exact path: the weights overwrote the scores, so recompute
+        // them (tile t is still in buffer i), raise each block's m to the
+        // exact row max, rescale O and l, and redo the weights.
+        scores(lb.k[i], valid[i], sa);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const float m_new = fmaxf(st[b].m, rowmax_half(sa[b]) * c);
+          const float alpha = __builtin_amdgcn_exp2f(st[b].m - m_new);
+          st[b].l *= alpha;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st[b].o[db][r] *= alpha;
+          st[b].m = m_new;
+        }
+        ls0 = exp_inplace(sa[0], c, st[0].m);
+        ls1 = exp_inplace(sa[1], c, st[1].m);
+      }
+      st[0].l += ls0;
+      st[1].l += ls1;
+    }
+    if (!hk) sync();
+    // Both groups are past this tile's barrier here, and both issue the copies
+    // of tile t+3 at the start of their MFMA phase.
+    if (t + 3 < t_end) valid[i3] = issue(t + 3, i3);
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const uint32_t vr[2] = {ho.v0, ho.v1};
+      pv_w64(lb.v[i], vr, sa, st);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // On the last tile the S^T of buffer i+1 is computed on stale data and dropped.
+    scores(lb.k[i1], more ? valid[i1] : kBlockN, sa);
+  };
+
+  for (int t = t_begin; t < t_end; t += 4) {
+    tile(t, 0);
+    if (t + 1 >= t_end) break;
+    tile(t + 1, 1);
+    if (t + 2 >= t_end) break;
+    tile(t + 2, 2);
+    if (t + 3 >= t_end) break;
+    tile(t + 3, 3);
+  }
+
+  // ---- merge of the two key halves, then the epilogue.  Wave w hands its
+  // block 1 to its partner w ^ 4 (for which it is block 0) through the LDS
+  // tile buffers (16 KB per wave, lane-major so that both sides' accesses are
+  // contiguous), with its m and per-lane l beside it, and finishes block 0.
+  __shared__ float2 xml[8][64];
+  // Exchange region of wave x (selects on wave-uniform bits, no table).
+  auto region = [&](int x) -> uint8_t* {
+    uint8_t* const k01 = (x & 1) ? lb.k[1] : lb.k[0];
+    uint8_t* const k23 = (x & 1) ? lb.k[3] : lb.k[2];
+    uint8_t* const v01 = (x & 1) ? lb.v[1] : lb.v[0];
+    uint8_t* const v23 = (x & 1) ? lb.v[3] : lb.v[2];
+    return (x & 4) ? ((x & 2) ? v23 : v01) : ((x & 2) ? k23 : k01);
+  };
+  const int lane = lane_now();
+  const int hl = lane >> 5;
+  __syncthreads();       // every wave is done with the tile buffers
+  {
+    float4* dst = reinterpret_cast<float4*>(region(w));
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& o = st[1].o[db];
+        dst[(db * 4 + g) * 64 + lane] = make_float4(o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]);
+      }
+    xml[w][lane] = make_float2(st[1].m, st[1].l);
+  }
+  __syncthreads();
+  const int pw = w ^ 4;
+  WaveState<D>& me = st[0];
+  {
+    const float4* src = reinterpret_cast<const float4*>(region(pw));
+    const float2 ml = xml[pw][lane];
+    const float M = fmaxf(me.m, ml.x);
+    const float wa = __builtin_amdgcn_exp2f(me.m - M), wb = __builtin_amdgcn_exp2f(ml.x - M);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 v = src[(db * 4 + g) * 64 + lane];
+        f32x16& o = me.o[db];
+        o[4 * g] = wa * o[4 * g] + wb * v.x;
+        o[4 * g + 1] = wa * o[4 * g + 1] + wb * v.y;
+        o[4 * g + 2] = wa * o[4 * g + 2] + wb * v.z;
+        o[4 * g + 3] = wa * o[4 * g + 3] + wb * v.w;
+      }
+    me.l = wa * me.l + wb * ml.y;
+    me.m = M;
+  }
+
+  const float l_tot = half_swap_sum(me.l);
+  const int row = (w & 3) * 64 + 32 * hk + (lane & 31);
+  const int q = qt * kBlockM + row;
+  if (q >= lq) return;
+  if (!slot) {
+    const float inv = 1.0f / l_tot;
+    __bf16* op = static_cast<__bf16*>(P.o) + (int64_t(q) * nh + h) * D + 4 * hl;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(me.o[db][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
+      }
+    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (me.m + log2f(l_tot)) * kLn2;
+  } else {
+    float* op = slot + row * D + 4 * hl;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& o = me.o[db];
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * g) =
+            make_float4(o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]);
+      }
+    if (hl == 0) {
+      slot[kBlockM * D + row] = me.m;
+      slot[kBlockM * D + kBlockM + row] = l_tot;
+    }
+  }
+}
+
 // Schedule of one call over n_wg persistent workgroups (one per CU).
 // Items run whole in full rounds (workgroup g takes item r*n_wg + g, so the
 // workgroups of an XCD stream one head's K/V in lockstep).  The rem items of
@@ -387,7 +769,7 @@ __host__ __device__ inline RemSplit rem_split(int n_items, int ntiles, int n_wg)
   return r;
 }
 
-template <int D, int NW>
+template <int D, int NW, bool W64>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch a) {
   // One array per tile buffer, so that the compiler sees the copies into one
   // buffer and the operand reads of another as disjoint.
@@ -431,7 +813,8 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch 
           slot = P.part + (int64_t(i) * 2 + 1) * a.slot_floats;
         }
       }
-      run_item<D, NW>(a, P, item, t_begin, t_end, slot, lb);
+      if constexpr (W64) run_item_w64<D>(a, P, item, t_begin, t_end, slot, lb);
+      else run_item<D, NW>(a, P, item, t_begin, t_end, slot, lb);
     }
   }
 }
@@ -742,8 +1125,8 @@ int dev_launch_attention(const AttnLaunch& a0, void* stream, Profiler* prof) {
   {
     Timed tm(prof, kAttn, s);
     const dim3 grid(a.n_wg), block(kAttnWaves * 64);
-    if (a.d == 64) hipLaunchKernelGGL((attn_bf16_kernel<64, kAttnWaves>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<128, kAttnWaves>), grid, block, 0, s, a);
+    if (a.d == 64) hipLaunchKernelGGL((attn_bf16_kernel<64, kAttnWaves, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<128, kAttnWaves, true>), grid, block, 0, s, a);
   }
   if (launch_ok()) return FF_E_HIP;
   {
