@@ -398,18 +398,17 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
 // 64 query rows per wave (head_dim 128).
 //
 // Every K or V^T operand read from LDS feeds two MFMAs (two blocks of 32
-// query rows): half the LDS read traffic per MFMA of the 32-row form, whose
-// operand reads alone would take the whole LDS read bandwidth (128 bytes per
-// clock per CU) at the matrix pipes' full rate.  The registers of 64 rows
-// (O^T 128, Q 64, scores 32, weights 16) leave no room for a second score
-// buffer, so a wave runs S^T, softmax and PV of its part of a tile in
-// sequence, and the two waves of each SIMD (w and w+4) interleave instead.
-// They hold the same 64 query rows: wave w < 4 takes keys 0..31 of every
-// 64-key tile, wave w+4 keys 32..63.  The one workgroup barrier per tile is
-// reached by the first group after its softmax and by the second before it,
-// which keeps one wave of each SIMD in its VALU phase while the other runs
-// its MFMAs (PV of this tile, then S^T of the next).  At the end the two
-// partial (m, l, O) of each row are merged through LDS.
+// query rows): half the LDS read instructions and bytes per MFMA of the
+// 32-row form.  The registers of 64 rows (O^T 128, Q 64, scores 32) leave no
+// room for a second score buffer, so the weights are packed in place over the
+// scores, a wave runs S^T, softmax and PV of its part of a tile in sequence,
+// and the two waves of each SIMD (w and w+4) interleave instead.  They hold
+// the same 64 query rows: wave w < 4 takes keys 0..31 of every 64-key tile,
+// wave w+4 keys 32..63.  The one workgroup barrier per tile is reached by the
+// first group after its softmax and by the second before it, which keeps one
+// wave of each SIMD in its VALU phase while the other runs its MFMAs (PV of
+// this tile, then S^T of the next).  At the end the two partial (m, l, O) of
+// each row are merged through LDS.
 // --------------------------------------------------------------------------
 
 // S^T of one key half for the wave's two row blocks.  kread is the lane's
