@@ -436,26 +436,54 @@ __device__ __forceinline__ void qk_w64(const uint8_t* kbuf, uint32_t kread, cons
   }
 }
 
-// O^T += V^T P^T over one key half; vread[j] is the lane's (biased) offset of
-// the half's V^T operand j, rows 0..31.  Reads one step ahead, as above.
-__device__ __forceinline__ void pv_w64(const uint8_t* vbuf, const uint32_t (&vread)[2], const f32x16 (&sp)[2],
-                                       WaveState<128> (&st)[2]) {
-  auto rd = [&](int k) {
-    const int j = k >> 2, db = k & 3;
-    return __builtin_bit_cast(
-        bf16x8, ld16(vbuf + (int32_t(vread[j]) - int32_t(kLdsBias)) + db * 32 * kBlockN * 2));
-  };
-  bf16x8 cur = rd(0);
+// mask_half on both blocks with per-register bit masks instead of compares
+// (no condition registers held across the sixteen selects).
+__device__ __forceinline__ void mask_pair(f32x16& a, f32x16& b, int limit, int hl) {
+  const int lim = limit - 8 * hl;
+  const uint32_t ninf = 0xff800000u;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int j = k >> 2, db = k & 3;
+  for (int r = 0; r < 16; ++r) {
+    const uint32_t keep = uint32_t(int32_t(16 * (r >> 3) + (r & 7) - lim) >> 31);
+    a[r] = __uint_as_float((__float_as_uint(a[r]) & keep) | (ninf & ~keep));
+    b[r] = __uint_as_float((__float_as_uint(b[r]) & keep) | (ninf & ~keep));
+  }
+}
+
+// The MFMA phase of one tile: PV of this tile (eight V^T operands of vbuf)
+// then S^T of the next (eight K operands of kbuf) as one operand stream, each
+// read one step ahead of its two MFMAs, so the first K read overlaps the last
+// PV MFMAs.  `first` is V^T operand 0, read by the caller beforehand.  The
+// scores s hold the weights (packed in place) on entry and the next tile's
+// scores on return.
+__device__ __forceinline__ void mfma_phase(const uint8_t* vbuf, const uint32_t (&vread)[2], const uint8_t* kbuf,
+                                           uint32_t kread, const bf16x8 (&qreg)[2][8], f32x16 (&s)[2],
+                                           WaveState<128> (&st)[2], bf16x8 first) {
+  auto rd = [&](int k) {
+    if (k < 8) {
+      const int j = k >> 2, db = k & 3;
+      return __builtin_bit_cast(bf16x8,
+                                ld16(vbuf + (int32_t(vread[j]) - int32_t(kLdsBias)) + db * 32 * kBlockN * 2));
+    }
+    return __builtin_bit_cast(bf16x8, ld16(kbuf + (kread ^ uint32_t((k - 8) << 5))));
+  };
+  const f32x16 zero = {};
+  bf16x8 cur = first;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
     bf16x8 nxt = cur;
-    if (k < 7) nxt = rd(k + 1);
+    if (k < 15) nxt = rd(k + 1);
     __builtin_amdgcn_sched_barrier(0);
-    st[0].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, j ? p_operand(sp[0], 1) : p_operand(sp[0], 0),
-                                                          st[0].o[db], 0, 0, 0);
-    st[1].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, j ? p_operand(sp[1], 1) : p_operand(sp[1], 0),
-                                                          st[1].o[db], 0, 0, 0);
+    if (k < 8) {
+      const int j = k >> 2, db = k & 3;
+      st[0].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, j ? p_operand(s[0], 1) : p_operand(s[0], 0),
+                                                            st[0].o[db], 0, 0, 0);
+      st[1].o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, j ? p_operand(s[1], 1) : p_operand(s[1], 0),
+                                                            st[1].o[db], 0, 0, 0);
+    } else {
+      const int ks = k - 8;
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qreg[0][ks], ks ? s[0] : zero, 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qreg[1][ks], ks ? s[1] : zero, 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
   }
@@ -582,11 +610,7 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
   auto scores = [&](const uint8_t* kbuf, int valid, f32x16 (&s)[2]) {
     qk_w64(kbuf, ho.k, qreg, s);
     const int limit = valid - 32 * hk;
-    if (limit < 32) {
-      const int hl = lane_now() >> 5;
-      mask_half(s[0], limit, hl);
-      mask_half(s[1], limit, hl);
-    }
+    if (limit < 32) mask_pair(s[0], s[1], limit, lane_now() >> 5);
   };
 
   f32x16 sa[2];
@@ -616,6 +640,9 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
       wg_barrier();
     };
     if (hk) sync();
+    // V^T operand 0 of this tile, read under the VALU phase (tile t landed
+    // before the previous barrier).
+    const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(lb.v[i] + (int32_t(ho.v0) - int32_t(kLdsBias))));
     {
       float ls0 = exp_inplace(sa[0], c, st[0].m), ls1 = exp_inplace(sa[1], c, st[1].m);
       if (__builtin_expect(__ballot(ls0 > kSumGuard || ls1 > kSumGuard) != 0, 0)) {
@@ -645,13 +672,16 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
     // of tile t+3 at the start of their MFMA phase.
     if (t + 3 < t_end) valid[i3] = issue(t + 3, i3);
     __builtin_amdgcn_sched_barrier(0);
+    // PV of this tile, then S^T of the next (on the last tile the S^T of
+    // buffer i+1 is computed on stale data and dropped).
     {
       const uint32_t vr[2] = {ho.v0, ho.v1};
-      pv_w64(lb.v[i], vr, sa, st);
+      mfma_phase(lb.v[i], vr, lb.k[i1], ho.k, qreg, sa, st, v0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // On the last tile the S^T of buffer i+1 is computed on stale data and dropped.
-    scores(lb.k[i1], more ? valid[i1] : kBlockN, sa);
+    if (more) {
+      const int limit = valid[i1] - 32 * hk;
+      if (limit < 32) mask_pair(sa[0], sa[1], limit, lane_now() >> 5);
+    }
   };
 
   for (int t = t_begin; t < t_end; t += 4) {
