@@ -16,7 +16,11 @@ constexpr int kMaxSeg = 24;        // renderer: <= 3 anchors + 8 history chunks 
                                    // planner: one per anchor latent (<= W_ctx)
 constexpr int kMaxPairs = 8;       // renderer calls fused into one launch
 constexpr int kMaxHistory = 8;
-constexpr int kBlockM = 256;       // query rows per attention work item (8 waves x 32)
+constexpr int kBlockM = 256;       // query rows per work item: attention at head_dim 64 (8 waves x 32)
+                                   // and the block-causal backward kernels
+constexpr int kBlockMW = 512;      // query rows per attention work item at head_dim 128 (8 waves x 64)
+// Query rows per work item of the bf16 attention kernel.
+constexpr int attn_block_m(int head_dim) { return head_dim == 128 ? kBlockMW : kBlockM; }
 constexpr int kMaxWg = 256;        // persistent attention workgroups at most (one per CU; the
                                    // device's CU count is queried at context creation)
 constexpr int kBlockN = 64;        // keys per LDS tile
@@ -35,7 +39,8 @@ struct SegTable {
 };
 
 // Attention work of one call ("pair" = chunk i at stage k).  Work item =
-// (head, 256-query tile); each item runs over all of the call's key tiles.
+// (head, query tile of attn_block_m(d) rows); each item runs over all of the
+// call's key tiles.
 // The (item x key tile) units of a call are split evenly and contiguously
 // over the persistent workgroups (stream-K); an item cut between workgroups
 // leaves partial results in `part` that the merge kernel combines.
@@ -136,9 +141,9 @@ struct BcLaunch {
 static_assert(sizeof(BcLaunch) <= 4096, "backward launch arguments exceed the kernel argument limit");
 
 // Fixed device scratch of ff_render_attend_static_scratch: the partial slots
-// of one call (two per persistent workgroup, each kBlockM rows of head_dim
-// (<= 128) fp32 values plus the row max and sum), 65 MiB.
-constexpr size_t kStaticScratchBytes = size_t(kMaxWg) * 2 * size_t(kBlockM) * (128 + 2) * 4;
+// of one call (two per persistent workgroup, each kBlockMW rows of head_dim
+// (<= 128) fp32 values plus the row max and sum), 130 MiB.
+constexpr size_t kStaticScratchBytes = size_t(kMaxWg) * 2 * size_t(kBlockMW) * (128 + 2) * 4;
 // Device address and size of that scratch on the current device; the
 // address is taken once per device.  Returns 0, or FF_E_HIP.
 int dev_static_scratch(void** ptr, size_t* bytes);

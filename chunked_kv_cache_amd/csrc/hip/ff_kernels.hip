@@ -59,10 +59,11 @@ constexpr float kSumGuard = 4096.0f;
 // global chunk each lane fetches.
 // --------------------------------------------------------------------------
 // Waves per work item: eight, two per SIMD.  Head dim 128 runs the 64-row
-// form (run_item_w64: waves w and w+4 share 64 query rows and split every
-// tile's keys, each K or V^T operand read feeds two MFMAs); head dim 64 runs
-// the 32-row form (run_item: wave w owns rows 32w..32w+31, one MFMA per
-// operand read, the S^T of the next half beside the softmax of this one).
+// form (run_item_r64: wave w owns rows 64w..64w+63 of a 512-row item and
+// walks both 32-key halves of every tile, each K or V^T operand read feeds
+// two MFMAs); head dim 64 runs the 32-row form (run_item: wave w owns rows
+// 32w..32w+31 of a 256-row item, one MFMA per operand read, the S^T of the
+// next half beside the softmax of this one).
 constexpr int kAttnWaves = 8;
 
 
@@ -395,20 +396,15 @@ __device__ __forceinline__ void run_item(const AttnLaunch& a, const PairLaunch& 
 }
 
 // --------------------------------------------------------------------------
-// 64 query rows per wave (head_dim 128).
+// 64 query rows per wave (head_dim 128): helpers.
 //
 // Every K or V^T operand read from LDS feeds two MFMAs (two blocks of 32
 // query rows): half the LDS read instructions and bytes per MFMA of the
 // 32-row form.  The registers of 64 rows (O^T 128, Q 64, scores 32) leave no
 // room for a second score buffer, so the weights are packed in place over the
-// scores, a wave runs S^T, softmax and PV of its part of a tile in sequence,
-// and the two waves of each SIMD (w and w+4) interleave instead.  They hold
-// the same 64 query rows: wave w < 4 takes keys 0..31 of every 64-key tile,
-// wave w+4 keys 32..63.  The one workgroup barrier per tile is reached by the
-// first group after its softmax and by the second before it, which keeps one
-// wave of each SIMD in its VALU phase while the other runs its MFMAs (PV of
-// this tile, then S^T of the next).  At the end the two partial (m, l, O) of
-// each row are merged through LDS.
+// scores of one 32-key half, a wave runs S^T, softmax and PV of a half in
+// sequence, and the two waves of each SIMD interleave instead (one in its
+// softmax while the other runs MFMAs).
 // --------------------------------------------------------------------------
 
 // S^T of one key half for the wave's two row blocks.  kread is the lane's
@@ -489,12 +485,6 @@ __device__ __forceinline__ void mfma_phase(const uint8_t* vbuf, const uint32_t (
   }
 }
 
-// Lower bound of a wave's reference max.  The second group's first half may
-// hold no valid key (a piece whose first tile has at most 32); its weights
-// against this bound overflow to infinity on the first valid key, which takes
-// the exact path of the softmax (rescale factor 0 on the empty O and l).
-constexpr float kMaxFloor = -1.0e30f;
-
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -510,45 +500,61 @@ __device__ __forceinline__ int lane_now() {
   return int(l);
 }
 
-// Operand offsets of one wave's key half (hk) for lane `lane`: K operand of
+// Operand offsets of key half 0 of a tile for lane `lane`: K operand of
 // k-step 0 (k-step ks at ^ (ks << 5)), V^T operands j = 0, 1 (+ kLdsBias).
 struct HalfOffsets {
   uint32_t k, v0, v1;
 };
-__device__ __forceinline__ HalfOffsets half_offsets(int lane, int hk) {
+__device__ __forceinline__ HalfOffsets half_offsets(int lane) {
   const int l32 = lane & 31, hl = lane >> 5;
   const int prow = (l32 & ~12) | ((l32 & 4) << 1) | ((l32 & 8) >> 1);
   HalfOffsets o;
-  o.k = uint32_t(hk * 32 * 128 * 2 + prow * 128 * 2 + ((hl ^ krow_swz<128>(prow)) << 4));
-  const uint32_t v = uint32_t(l32 * kBlockN * 2 + (((4 * hk + hl) ^ vrow_swz(l32)) << 4)) + kLdsBias;
+  o.k = uint32_t(prow * 128 * 2 + ((hl ^ krow_swz<128>(prow)) << 4));
+  const uint32_t v = uint32_t(l32 * kBlockN * 2 + ((hl ^ vrow_swz(l32)) << 4)) + kLdsBias;
   o.v0 = opaque(v);
   o.v1 = opaque(v ^ 32u);
   return o;
 }
 
+// --------------------------------------------------------------------------
+// 512 query rows per workgroup (head_dim 128): every wave owns 64 rows of its
+// own and walks both 32-key halves of each 64-key tile, so one K/V tile in
+// LDS serves twice the query rows of the form above and the global -> LDS
+// copies per FLOP are halved.  The registers per wave are those of the form
+// above (one half's scores at a time, weights packed in place).  A wave runs,
+// per tile t: softmax of half 0 (V0), PV of half 0 + S^T of half 1 (M0),
+// softmax of half 1 (V1), PV of half 1 + S^T of half 0 of tile t+1 (M1).
+// The barrier of a tile that orders the copies (tile t+1 landed, tile t-1's
+// buffer free) comes before M1: waves 0..3 reach it after V1 and waves 4..7
+// before V1; a second one before M0 (after V0, resp. before it) keeps the
+// pairing.  So one wave of each SIMD is in a VALU phase while the other runs
+// MFMAs.
+// Each wave finishes its own rows: no merge between waves.
+// --------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaunch& P, int item, int t_begin,
+__device__ __forceinline__ void run_item_r64(const AttnLaunch& a, const PairLaunch& P, int item, int t_begin,
                                              int t_end, float* slot, const LdsBufs& lb) {
-  static_assert(D == 128, "the 64-row form is laid out for head_dim 128");
+  static_assert(D == 128, "the 512-row form is laid out for head_dim 128");
   constexpr int NW = 8;
   constexpr int KS = D / 16;
+  constexpr int BM = kBlockMW;
   constexpr int kDma = TileCfg<D, NW>::kDmaPerTile;   // per wave
   static_assert(TileCfg<D, NW>::kKBlocks == 2 && TileCfg<D, NW>::kVBlocks == 2, "two copies of each per wave");
+  constexpr uint32_t kHalfK = 32 * D * 2;    // K rows of key half 1: byte offset in a K tile
+  constexpr uint32_t kHalfV = 4u << 4;       // V^T chunk of key half 1: XOR on the operand offset
   const int nh = a.nh, lq = a.lq;
   const int qt = item % a.n_qtiles;
   const int h = item / a.n_qtiles;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hk = w >> 2;                         // key half of every tile
+  const int grp = w >> 2;                    // barrier group
 
-  // Register block b holds rows 64 * (w & 3) + 32 * (b ^ hk) + lane % 32:
-  // each wave keeps block 0 to the end and hands block 1 to its partner, whose
-  // block 0 they are.
+  // Register block b holds rows 64 * w + 32 * b + lane % 32.
   bf16x8 qreg[2][KS];
   {
     const int lane = lane_now();
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int q = qt * kBlockM + (w & 3) * 64 + 32 * (b ^ hk) + (lane & 31);
+      const int q = qt * BM + w * 64 + 32 * b + (lane & 31);
       const bool ok = q < lq;
       const __bf16* qp = static_cast<const __bf16*>(P.q) + (int64_t(ok ? q : 0) * nh + h) * D + 8 * (lane >> 5);
 #pragma unroll
@@ -571,8 +577,8 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
     st[b].l = 0.f;
   }
 
-  // The lane offsets of the tile copies are used once per tile: they wait in
-  // LDS (each lane reads back only what it wrote), not in registers.
+  // The lane offsets of the tile copies wait in LDS (each lane reads back
+  // only what it wrote), not in registers.
   __shared__ u32x2 kdo[NW * 64], vdo[NW * 64];
   {
     const int lane = lane_now();
@@ -604,17 +610,43 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
     dma16(rv, vo[1], lb.v[i] + (w * 2 + 1) * 1024);
     return min(kBlockN, cur.n - o);
   };
-  // S^T of this wave's half of the tile in kbuf, keys at or past `valid`
-  // masked (a rarely taken branch).
-  const HalfOffsets ho = half_offsets(lane_now(), hk);
-  auto scores = [&](const uint8_t* kbuf, int valid, f32x16 (&s)[2]) {
-    qk_w64(kbuf, ho.k, qreg, s);
-    const int limit = valid - 32 * hk;
+  // Operand offsets of key half 0 (half 1: K at + kHalfK, V^T at ^ kHalfV).
+  const HalfOffsets ho = half_offsets(lane_now());
+  // S^T of key half `hf` of the tile in kbuf, keys at or past `valid` masked
+  // (a rarely taken branch).
+  auto scores = [&](const uint8_t* kbuf, int valid, int hf, f32x16 (&s)[2]) {
+    qk_w64(kbuf + (hf ? kHalfK : 0u), ho.k, qreg, s);
+    const int limit = valid - 32 * hf;
     if (limit < 32) mask_pair(s[0], s[1], limit, lane_now() >> 5);
   };
-
+  // Softmax of one half in place over its scores (sa), the lane sums added to
+  // l.  Rare exact path: the weights overwrote the scores, so recompute them
+  // (the tile is still in buffer i), raise each block's m to the exact row
+  // max, rescale O and l, and redo the weights.
   f32x16 sa[2];
   int valid[4];
+  auto softmax = [&](int i, int hf) {
+    float ls0 = exp_inplace(sa[0], c, st[0].m), ls1 = exp_inplace(sa[1], c, st[1].m);
+    if (__builtin_expect(__ballot(ls0 > kSumGuard || ls1 > kSumGuard) != 0, 0)) {
+      scores(lb.k[i], valid[i], hf, sa);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const float m_new = fmaxf(st[b].m, rowmax_half(sa[b]) * c);
+        const float alpha = __builtin_amdgcn_exp2f(st[b].m - m_new);
+        st[b].l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) st[b].o[db][r] *= alpha;
+        st[b].m = m_new;
+      }
+      ls0 = exp_inplace(sa[0], c, st[0].m);
+      ls1 = exp_inplace(sa[1], c, st[1].m);
+    }
+    st[0].l += ls0;
+    st[1].l += ls1;
+  };
+
   __syncthreads();       // the previous piece's reads of the buffers are done
   valid[0] = issue(t_begin, 0);
   if (t_begin + 1 < t_end) valid[1] = issue(t_begin + 1, 1);
@@ -623,63 +655,52 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
   else if (t_begin + 1 < t_end) wait_dma_but<kDma>();
   else wait_dma();
   wg_barrier();
-  scores(lb.k[0], valid[0], sa);
+  scores(lb.k[0], valid[0], 0, sa);
+  // The first half of a piece holds at least one valid key, so m is finite.
 #pragma unroll
-  for (int b = 0; b < 2; ++b) st[b].m = fmaxf(rowmax_half(sa[b]) * c, kMaxFloor);
+  for (int b = 0; b < 2; ++b) st[b].m = rowmax_half(sa[b]) * c;
 
   // Tile t is in buffer i (landed); i+1 holds tile t+1 and i+2 tile t+2 (both
   // may still be landing); i+3 is free for tile t+3 once every wave is past
-  // this tile's barrier (indices mod 4).  Every wave passes one barrier per
-  // tile.  Invariant at entry: sa = masked scores of this wave's half of tile t.
+  // this tile's barrier (indices mod 4).  Invariant at entry: sa = masked
+  // scores of half 0 of tile t.
+  const uint32_t vr0[2] = {ho.v0, ho.v1};
+  const uint32_t vr1[2] = {ho.v0 ^ kHalfV, ho.v1 ^ kHalfV};
   auto tile = [&](int t, int i) {
     const int i1 = (i + 1) & 3, i3 = (i + 3) & 3;
     const bool more = t + 1 < t_end;
+    // V0, then M0: PV of half 0, S^T of half 1 (tile t landed before the
+    // previous barrier).  A second barrier per tile paces the two groups
+    // (waves 0..3 reach it after V0, waves 4..7 before it): with one barrier
+    // per tile their phases drift into each other.
+    {
+      if (grp) wg_barrier();
+      const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(lb.v[i] + (int32_t(ho.v0) - int32_t(kLdsBias))));
+      softmax(i, 0);
+      if (!grp) wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_phase(lb.v[i], vr0, lb.k[i] + kHalfK, ho.k, qreg, sa, st, v0);
+      const int limit = valid[i] - 32;
+      if (limit < 32) mask_pair(sa[0], sa[1], limit, lane_now() >> 5);
+    }
     auto sync = [&] {
       if (more && t + 2 < t_end) wait_dma_but<kDma>();   // tile t+1 landed, t+2 may fly
       else wait_dma();
       wg_barrier();
     };
-    if (hk) sync();
-    // V^T operand 0 of this tile, read under the VALU phase (tile t landed
-    // before the previous barrier).
-    const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(lb.v[i] + (int32_t(ho.v0) - int32_t(kLdsBias))));
-    {
-      float ls0 = exp_inplace(sa[0], c, st[0].m), ls1 = exp_inplace(sa[1], c, st[1].m);
-      if (__builtin_expect(__ballot(ls0 > kSumGuard || ls1 > kSumGuard) != 0, 0)) {
-        // Rare exact path: the weights overwrote the scores, so recompute
-        // them (tile t is still in buffer i), raise each block's m to the
-        // exact row max, rescale O and l, and redo the weights.
-        scores(lb.k[i], valid[i], sa);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const float m_new = fmaxf(st[b].m, rowmax_half(sa[b]) * c);
-          const float alpha = __builtin_amdgcn_exp2f(st[b].m - m_new);
-          st[b].l *= alpha;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st[b].o[db][r] *= alpha;
-          st[b].m = m_new;
-        }
-        ls0 = exp_inplace(sa[0], c, st[0].m);
-        ls1 = exp_inplace(sa[1], c, st[1].m);
-      }
-      st[0].l += ls0;
-      st[1].l += ls1;
-    }
-    if (!hk) sync();
+    if (grp) sync();
+    // V1, then M1: PV of half 1, S^T of half 0 of tile t+1 (on the last tile
+    // computed on stale data and dropped).
+    const bf16x8 v0 = __builtin_bit_cast(bf16x8, ld16(lb.v[i] + (int32_t(ho.v0 ^ kHalfV) - int32_t(kLdsBias))));
+    softmax(i, 1);
+    if (!grp) sync();
     // Both groups are past this tile's barrier here, and both issue the copies
-    // of tile t+3 at the start of their MFMA phase.
+    // of tile t+3 at the start of M1.
     if (t + 3 < t_end) valid[i3] = issue(t + 3, i3);
     __builtin_amdgcn_sched_barrier(0);
-    // PV of this tile, then S^T of the next (on the last tile the S^T of
-    // buffer i+1 is computed on stale data and dropped).
-    {
-      const uint32_t vr[2] = {ho.v0, ho.v1};
-      mfma_phase(lb.v[i], vr, lb.k[i1], ho.k, qreg, sa, st, v0);
-    }
+    mfma_phase(lb.v[i], vr1, lb.k[i1], ho.k, qreg, sa, st, v0);
     if (more) {
-      const int limit = valid[i1] - 32 * hk;
+      const int limit = valid[i1];
       if (limit < 32) mask_pair(sa[0], sa[1], limit, lane_now() >> 5);
     }
   };
@@ -694,86 +715,43 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
     tile(t + 3, 3);
   }
 
-  // ---- merge of the two key halves, then the epilogue.  Wave w hands its
-  // block 1 to its partner w ^ 4 (for which it is block 0) through the LDS
-  // tile buffers (16 KB per wave, lane-major so that both sides' accesses are
-  // contiguous), with its m and per-lane l beside it, and finishes block 0.
-  __shared__ float2 xml[8][64];
-  // Exchange region of wave x (selects on wave-uniform bits, no table).
-  auto region = [&](int x) -> uint8_t* {
-    uint8_t* const k01 = (x & 1) ? lb.k[1] : lb.k[0];
-    uint8_t* const k23 = (x & 1) ? lb.k[3] : lb.k[2];
-    uint8_t* const v01 = (x & 1) ? lb.v[1] : lb.v[0];
-    uint8_t* const v23 = (x & 1) ? lb.v[3] : lb.v[2];
-    return (x & 4) ? ((x & 2) ? v23 : v01) : ((x & 2) ? k23 : k01);
-  };
   const int lane = lane_now();
   const int hl = lane >> 5;
-  __syncthreads();       // every wave is done with the tile buffers
-  {
-    float4* dst = reinterpret_cast<float4*>(region(w));
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int b = 0; b < 2; ++b) {
+    const WaveState<D>& me = st[b];
+    const float l_tot = half_swap_sum(me.l);
+    const int row = w * 64 + 32 * b + (lane & 31);
+    const int q = qt * BM + row;
+    if (q < lq) {
+      if (!slot) {
+        const float inv = 1.0f / l_tot;
+        __bf16* op = static_cast<__bf16*>(P.o) + (int64_t(q) * nh + h) * D + 4 * hl;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& o = st[1].o[db];
-        dst[(db * 4 + g) * 64 + lane] = make_float4(o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]);
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            bf16x4 ov;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(me.o[db][4 * g + e] * inv);
+            *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
+          }
+        if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (me.m + log2f(l_tot)) * kLn2;
+      } else {
+        float* op = slot + row * D + 4 * hl;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& o = me.o[db];
+            *reinterpret_cast<float4*>(op + 32 * db + 8 * g) =
+                make_float4(o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]);
+          }
+        if (hl == 0) {
+          slot[BM * D + row] = me.m;
+          slot[BM * D + BM + row] = l_tot;
+        }
       }
-    xml[w][lane] = make_float2(st[1].m, st[1].l);
-  }
-  __syncthreads();
-  const int pw = w ^ 4;
-  WaveState<D>& me = st[0];
-  {
-    const float4* src = reinterpret_cast<const float4*>(region(pw));
-    const float2 ml = xml[pw][lane];
-    const float M = fmaxf(me.m, ml.x);
-    const float wa = __builtin_amdgcn_exp2f(me.m - M), wb = __builtin_amdgcn_exp2f(ml.x - M);
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 v = src[(db * 4 + g) * 64 + lane];
-        f32x16& o = me.o[db];
-        o[4 * g] = wa * o[4 * g] + wb * v.x;
-        o[4 * g + 1] = wa * o[4 * g + 1] + wb * v.y;
-        o[4 * g + 2] = wa * o[4 * g + 2] + wb * v.z;
-        o[4 * g + 3] = wa * o[4 * g + 3] + wb * v.w;
-      }
-    me.l = wa * me.l + wb * ml.y;
-    me.m = M;
-  }
-
-  const float l_tot = half_swap_sum(me.l);
-  const int row = (w & 3) * 64 + 32 * hk + (lane & 31);
-  const int q = qt * kBlockM + row;
-  if (q >= lq) return;
-  if (!slot) {
-    const float inv = 1.0f / l_tot;
-    __bf16* op = static_cast<__bf16*>(P.o) + (int64_t(q) * nh + h) * D + 4 * hl;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = (__bf16)(me.o[db][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * g) = ov;
-      }
-    if (P.lse && hl == 0) P.lse[int64_t(h) * lq + q] = (me.m + log2f(l_tot)) * kLn2;
-  } else {
-    float* op = slot + row * D + 4 * hl;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& o = me.o[db];
-        *reinterpret_cast<float4*>(op + 32 * db + 8 * g) =
-            make_float4(o[4 * g], o[4 * g + 1], o[4 * g + 2], o[4 * g + 3]);
-      }
-    if (hl == 0) {
-      slot[kBlockM * D + row] = me.m;
-      slot[kBlockM * D + kBlockM + row] = l_tot;
     }
   }
 }
@@ -781,21 +759,34 @@ __device__ __forceinline__ void run_item_w64(const AttnLaunch& a, const PairLaun
 // Schedule of one call over n_wg persistent workgroups (one per CU).
 // Items run whole in full rounds (workgroup g takes item r*n_wg + g, so the
 // workgroups of an XCD stream one head's K/V in lockstep).  The rem items of
-// the last, partial round are cut at key tile F: workgroup g < rem runs item g
-// over [0, F) and the spare workgroups run the tails [F, ntiles), k items each,
-// with F chosen so that k tails take about as long as one head: F =
-// ceil(k * ntiles / (k + 1)).  Cut items leave two partials for the merge.
-struct RemSplit {
-  int full, rem, k, F;
+// the last, partial round form one sequence of rem * ntiles (item, key tile)
+// units, item-major, cut into n_wg contiguous ranges of equal length (to one
+// tile): workgroup g runs units [lo(g), lo(g+1)).  A range holds at most
+// one item's worth of units, so it covers parts of at most two items (the
+// end of one, the start of the next).  Every last-round piece leaves a
+// partial (O, m, l) in slot 2g (the first piece of workgroup g) or 2g + 1
+// (its second), and the merge kernel combines an item's pieces in workgroup
+// order (one piece when the item fell into a single range).
+struct LastRound {
+  int full, rem;
+  int64_t units;                   // rem * ntiles
 };
-__host__ __device__ inline RemSplit rem_split(int n_items, int ntiles, int n_wg) {
-  RemSplit r;
+__host__ __device__ inline LastRound last_round(int n_items, int ntiles, int n_wg) {
+  LastRound r;
   r.full = n_items / n_wg;
   r.rem = n_items % n_wg;
-  r.k = r.rem ? (r.rem + (n_wg - r.rem) - 1) / (n_wg - r.rem) : 0;
-  r.F = r.rem ? (r.k * ntiles + r.k) / (r.k + 1) : ntiles;   // ceil(k*ntiles/(k+1))
-  if (r.F > ntiles) r.F = ntiles;
+  r.units = int64_t(r.rem) * ntiles;
   return r;
+}
+__host__ __device__ inline int64_t range_lo(const LastRound& r, int g, int n_wg) {
+  return r.units * g / n_wg;
+}
+// The workgroup whose range holds unit u (u < units).
+__host__ __device__ inline int range_of(const LastRound& r, int64_t u, int n_wg) {
+  int g = int(u * n_wg / r.units);
+  while (g + 1 < n_wg && range_lo(r, g + 1, n_wg) <= u) ++g;
+  while (g > 0 && range_lo(r, g, n_wg) > u) --g;
+  return g;
 }
 
 template <int D, int NW, bool W64>
@@ -816,44 +807,39 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch 
   const int g = xcd_remap(blockIdx.x, gridDim.x, a.n_xcd);
   for (int p = 0; p < a.n_pairs; ++p) {
     const PairLaunch& P = a.pair[p];
-    const RemSplit rs = rem_split(P.n_items, P.ntiles, a.n_wg);
-    const int base = rs.full * a.n_wg;
-    const bool cut = rs.F < P.ntiles;
-    // Pieces of this workgroup: rs.full whole items, then its last-round share.
-    int n_last = 0, first_tail = 0;
-    if (g < rs.rem) {
-      n_last = 1;
-    } else if (cut) {
-      first_tail = (g - rs.rem) * rs.k;
-      n_last = max(0, min(rs.rem, first_tail + rs.k) - first_tail);
-    }
-    for (int u = 0; u < rs.full + n_last; ++u) {
-      int item = u * a.n_wg + g, t_begin = 0, t_end = P.ntiles;
+    const LastRound lr = last_round(P.n_items, P.ntiles, a.n_wg);
+    const int64_t lo = lr.rem ? range_lo(lr, g, a.n_wg) : 0, hi = lr.rem ? range_lo(lr, g + 1, a.n_wg) : 0;
+    // Pieces of this workgroup: lr.full whole items, then its last-round range
+    // (one call site, so the item body is inlined once).
+    int u = 0;
+    for (int64_t pos = lo;;) {
+      int item, t_begin = 0, t_end = P.ntiles;
       float* slot = nullptr;
-      if (u >= rs.full) {
-        if (g < rs.rem) {
-          item = base + g;
-          t_end = rs.F;
-          if (cut) slot = P.part + int64_t(g) * 2 * a.slot_floats;
-        } else {
-          const int i = first_tail + (u - rs.full);
-          item = base + i;
-          t_begin = rs.F;
-          slot = P.part + (int64_t(i) * 2 + 1) * a.slot_floats;
-        }
+      if (u < lr.full) {
+        item = u * a.n_wg + g;
+        ++u;
+      } else if (pos < hi) {
+        const int x = int(pos / P.ntiles);
+        t_begin = int(pos - int64_t(x) * P.ntiles);
+        t_end = int(min(int64_t(P.ntiles), hi - int64_t(x) * P.ntiles));
+        slot = P.part + (int64_t(g) * 2 + (pos == lo ? 0 : 1)) * a.slot_floats;
+        item = lr.full * a.n_wg + x;
+        pos = int64_t(x) * P.ntiles + t_end;
+      } else {
+        break;
       }
-      if constexpr (W64) run_item_w64<D>(a, P, item, t_begin, t_end, slot, lb);
+      if constexpr (W64) run_item_r64<D>(a, P, item, t_begin, t_end, slot, lb);
       else run_item<D, NW>(a, P, item, t_begin, t_end, slot, lb);
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// Merge of the items cut in the last round: O = sum_j 2^(m_j - M) O_j /
-// sum_j 2^(m_j - M) l_j over the head piece (j = 0) and the tail piece (j = 1).
-// One block per 32 query rows of a cut item and call; D/4 consecutive threads
-// share a query row, each taking 4 head-dim values, so partial reads and O
-// writes are coalesced.
+// Merge of the items of the last round: O = sum_j 2^(m_j - M) O_j /
+// sum_j 2^(m_j - M) l_j over the item's pieces j, in workgroup order.  One
+// block per 32 query rows of a last-round item and call; D/4 consecutive
+// threads share a query row, each taking 4 head-dim values, so partial reads
+// and O writes are coalesced.
 // --------------------------------------------------------------------------
 constexpr int kMergeRows = 32;   // query rows per merge block
 
@@ -861,35 +847,70 @@ template <int D>
 __global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
   constexpr int TPR = D / 4;                     // threads per row
   constexpr int RPP = 256 / TPR;                 // rows per pass
+  constexpr int BM = attn_block_m(D);            // query rows of an item
   const PairLaunch& P = a.pair[blockIdx.y];
-  const RemSplit rs = rem_split(P.n_items, P.ntiles, a.n_wg);
-  const int i = blockIdx.x / (kBlockM / kMergeRows);
-  if (i >= rs.rem || rs.F >= P.ntiles) return;
-  const int item = rs.full * a.n_wg + i;
+  const LastRound lr = last_round(P.n_items, P.ntiles, a.n_wg);
+  const int x = blockIdx.x / (BM / kMergeRows);
+  if (x >= lr.rem) return;
+  const int item = lr.full * a.n_wg + x;
   const int qt = item % a.n_qtiles, h = item / a.n_qtiles;
-  const float* s0 = P.part + int64_t(i) * 2 * a.slot_floats;
-  const float* s1 = s0 + a.slot_floats;
+  // Pieces: the non-empty ranges of workgroups g0..g1; the piece of g0 is its
+  // second unless its range starts at this item.
+  const int64_t u0 = int64_t(x) * P.ntiles, u1 = u0 + P.ntiles - 1;
+  const int g0 = range_of(lr, u0, a.n_wg), g1 = range_of(lr, u1, a.n_wg);
+  const int first = range_lo(lr, g0, a.n_wg) < u0 ? 1 : 0;
   const int c4 = threadIdx.x % TPR;
-  const int r0 = (blockIdx.x % (kBlockM / kMergeRows)) * kMergeRows + threadIdx.x / TPR;
+  const int r0 = (blockIdx.x % (BM / kMergeRows)) * kMergeRows + threadIdx.x / TPR;
+  constexpr int NP = kMergeRows / RPP;           // rows per thread
+  float M[NP], L[NP];
+  float4 acc[NP];
 #pragma unroll
-  for (int pass = 0; pass < kMergeRows / RPP; ++pass) {
-    const int row = r0 + pass * RPP;
-    const int q = qt * kBlockM + row;
+  for (int j = 0; j < NP; ++j) {
+    M[j] = -INFINITY;
+    L[j] = 0.f;
+    acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  // Two sweeps over the pieces (the row max, then the weighted sums); the
+  // rows past lq read the slots' unwritten rows and are not stored.
+  for (int sweep = 0; sweep < 2; ++sweep) {
+    int64_t lo_g = range_lo(lr, g0, a.n_wg);
+    for (int g = g0; g <= g1; ++g) {
+      const int64_t lo_n = range_lo(lr, g + 1, a.n_wg);
+      const bool empty = lo_g == lo_n;
+      lo_g = lo_n;
+      if (empty) continue;
+      const float* sp = P.part + (int64_t(g) * 2 + (g == g0 ? first : 0)) * a.slot_floats;
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int row = r0 + j * RPP;
+        const float m = sp[BM * D + row];
+        if (sweep == 0) {
+          M[j] = fmaxf(M[j], m);
+        } else {
+          const float wj = __builtin_amdgcn_exp2f(m - M[j]);
+          L[j] += wj * sp[BM * D + BM + row];
+          const float4 v = reinterpret_cast<const float4*>(sp + row * D)[c4];
+          acc[j].x += wj * v.x;
+          acc[j].y += wj * v.y;
+          acc[j].z += wj * v.z;
+          acc[j].w += wj * v.w;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int row = r0 + j * RPP;
+    const int q = qt * BM + row;
     if (q >= a.lq) break;
-    const float m0 = s0[kBlockM * D + row], m1 = s1[kBlockM * D + row];
-    const float M = fmaxf(m0, m1);
-    const float w0 = __builtin_amdgcn_exp2f(m0 - M), w1 = __builtin_amdgcn_exp2f(m1 - M);
-    const float L = w0 * s0[kBlockM * D + kBlockM + row] + w1 * s1[kBlockM * D + kBlockM + row];
-    const float inv = 1.0f / L;
-    const float4 x = reinterpret_cast<const float4*>(s0 + row * D)[c4];
-    const float4 y = reinterpret_cast<const float4*>(s1 + row * D)[c4];
+    const float inv = 1.0f / L[j];
     bf16x4 ov;
-    ov[0] = (__bf16)((w0 * x.x + w1 * y.x) * inv);
-    ov[1] = (__bf16)((w0 * x.y + w1 * y.y) * inv);
-    ov[2] = (__bf16)((w0 * x.z + w1 * y.z) * inv);
-    ov[3] = (__bf16)((w0 * x.w + w1 * y.w) * inv);
+    ov[0] = (__bf16)(acc[j].x * inv);
+    ov[1] = (__bf16)(acc[j].y * inv);
+    ov[2] = (__bf16)(acc[j].z * inv);
+    ov[3] = (__bf16)(acc[j].w * inv);
     *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(P.o) + (int64_t(q) * a.nh + h) * D + 4 * c4) = ov;
-    if (P.lse && c4 == 0) P.lse[int64_t(h) * a.lq + q] = (M + log2f(L)) * kLn2;
+    if (P.lse && c4 == 0) P.lse[int64_t(h) * a.lq + q] = (M[j] + log2f(L[j])) * kLn2;
   }
 }
 
@@ -1162,11 +1183,11 @@ int dev_launch_attention(const AttnLaunch& a0, void* stream, Profiler* prof) {
     Timed tm(prof, kMerge, s);
     int max_rem = 0;
     for (int p = 0; p < a.n_pairs; ++p) {
-      const RemSplit rs = rem_split(a.pair[p].n_items, a.pair[p].ntiles, a.n_wg);
-      if (rs.F < a.pair[p].ntiles && rs.rem > max_rem) max_rem = rs.rem;
+      const LastRound lr = last_round(a.pair[p].n_items, a.pair[p].ntiles, a.n_wg);
+      if (lr.rem > max_rem) max_rem = lr.rem;
     }
     if (max_rem == 0) return 0;
-    dim3 grid(unsigned(max_rem * (kBlockM / kMergeRows)), unsigned(a.n_pairs));
+    dim3 grid(unsigned(max_rem * (attn_block_m(a.d) / kMergeRows)), unsigned(a.n_pairs));
     if (a.d == 64) hipLaunchKernelGGL(merge_pieces_kernel<64>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(merge_pieces_kernel<128>, grid, dim3(256), 0, s, a);
   }

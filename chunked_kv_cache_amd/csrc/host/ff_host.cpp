@@ -87,7 +87,7 @@ Layout layout_of(const ff_shape* s, int S, int H) {
   // Split-item partial slots (bf16 path): 2 per workgroup, in one region per
   // stage and one for planner calls, so that calls of different stages (or a
   // planner call) may run concurrently on different streams.
-  L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(kBlockM) * (d + 2) * 4) : 0;
+  L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(attn_block_m(d)) * (d + 2) * 4) : 0;
   L.part_off = L.slot_off + size_t(S) * size_t(H + 1) * L.slot_block;
   L.total = L.part_off + size_t(S + 1) * part_region_bytes(L.part_slot);
   return L;
@@ -239,7 +239,7 @@ void fill_attention(const ff_ctx* c, int n_pairs, const int* ks, const ff_key_so
   a->nh = c->shape.n_heads;
   a->d = c->shape.head_dim;
   a->lq = int32_t(lq);
-  a->n_qtiles = int32_t((lq + kBlockM - 1) / kBlockM);
+  a->n_qtiles = int32_t((lq + attn_block_m(a->d) - 1) / attn_block_m(a->d));
   a->dtype = c->shape.dtype;
   a->scale = float(1.0 / std::sqrt(double(c->shape.head_dim)));
   a->slot_floats = int64_t(c->part_slot_bytes / 4);
@@ -671,7 +671,7 @@ BcLayout bc_layout_of(const ff_shape* s) {
   L.qq_chunk = take(size_t(L.n_chunk) * L.blk_chunk);
   L.gg_chunk = take(size_t(L.n_chunk) * L.blk_chunk);
   L.stats = take(size_t(L.n_chunk) * nh * lq * 8);
-  L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(kBlockM) * (d + 2) * 4) : 0;
+  L.part_slot = s->dtype == FF_BF16 ? align_up(size_t(attn_block_m(d)) * (d + 2) * 4) : 0;
   L.part = take(size_t(kMaxPairs) * part_region_bytes(L.part_slot));
   L.total = off;
   return L;
@@ -818,7 +818,7 @@ ff_status ff_bc_forward(ff_bc* b, const void* Ka, const void* Va, const void* Q,
     a.nh = b->shape.n_heads;
     a.d = b->shape.head_dim;
     a.lq = int32_t(b->Lq);
-    a.n_qtiles = int32_t((b->Lq + kBlockM - 1) / kBlockM);
+    a.n_qtiles = int32_t((b->Lq + attn_block_m(a.d) - 1) / attn_block_m(a.d));
     a.dtype = b->shape.dtype;
     a.scale = float(1.0 / std::sqrt(double(b->shape.head_dim)));
     a.slot_floats = int64_t(b->part_slot / 4);

@@ -467,7 +467,7 @@ def test_partial_regions_are_per_stage():
     try:
         _, slot_block, slot_off = _layout(cfg)
         part_off = slot_off + 3 * 6 * slot_block
-        part_slot = (256 * 130 * 4 + 255) // 256 * 256
+        part_slot = (512 * 130 * 4 + 255) // 256 * 256      # 512 query rows per item at head_dim 128
         region = 256 * 2 * part_slot
         assert hc.need == part_off + 4 * region
         _publish_anchors(hc)
