@@ -759,34 +759,51 @@ __device__ __forceinline__ void run_item_r64(const AttnLaunch& a, const PairLaun
 // Schedule of one call over n_wg persistent workgroups (one per CU).
 // Items run whole in full rounds (workgroup g takes item r*n_wg + g, so the
 // workgroups of an XCD stream one head's K/V in lockstep).  The rem items of
-// the last, partial round form one sequence of rem * ntiles (item, key tile)
-// units, item-major, cut into n_wg contiguous ranges of equal length (to one
-// tile): workgroup g runs units [lo(g), lo(g+1)).  A range holds at most
-// one item's worth of units, so it covers parts of at most two items (the
-// end of one, the start of the next).  Every last-round piece leaves a
-// partial (O, m, l) in slot 2g (the first piece of workgroup g) or 2g + 1
-// (its second), and the merge kernel combines an item's pieces in workgroup
-// order (one piece when the item fell into a single range).
+// the last, partial round are cut along their key tiles into m = n_wg / rem
+// levels and a remainder: level j is the tile range [F(j), F(j+1)) of every
+// item, run by workgroups j*rem .. j*rem + rem-1 (again in lockstep, one item
+// each); the remainders [F(m), ntiles) of all items, item-major, are cut into
+// equal contiguous ranges for the n_wg - m*rem leftover workgroups, each of
+// which runs several short pieces.  F(j) = j*rem*(ntiles + c)/n_wg with c =
+// kPieceCost tiles, the cost of a piece's start and partial write, so that a
+// level piece and a leftover range (with its pieces) take about as long.
+// Every piece leaves a partial (O, m, l) in its own slot (level piece of
+// workgroup g: slot g; remainder piece of item x in leftover range k: slot
+// m*rem + x + k, below 2*n_wg) and the merge kernel combines an item's pieces
+// in key order.
+constexpr int kPieceCost = 6;
 struct LastRound {
-  int full, rem;
-  int64_t units;                   // rem * ntiles
+  int full, rem, m, left, ntiles, n_wg;
+  int fm;                          // F(m): first tile of the remainders
+  int r;                           // remainder tiles per item
 };
+__host__ __device__ inline int level_start(const LastRound& lr, int j) {
+  if (j >= lr.m && lr.left == 0) return lr.ntiles;
+  const int64_t f = int64_t(j) * lr.rem * (lr.ntiles + kPieceCost) / lr.n_wg;
+  return f < lr.ntiles ? int(f) : lr.ntiles;
+}
 __host__ __device__ inline LastRound last_round(int n_items, int ntiles, int n_wg) {
-  LastRound r;
-  r.full = n_items / n_wg;
-  r.rem = n_items % n_wg;
-  r.units = int64_t(r.rem) * ntiles;
-  return r;
+  LastRound lr;
+  lr.full = n_items / n_wg;
+  lr.rem = n_items % n_wg;
+  lr.ntiles = ntiles;
+  lr.n_wg = n_wg;
+  lr.m = lr.rem ? n_wg / lr.rem : 0;
+  lr.left = n_wg - lr.m * lr.rem;
+  lr.fm = lr.rem ? level_start(lr, lr.m) : ntiles;
+  lr.r = ntiles - lr.fm;
+  return lr;
 }
-__host__ __device__ inline int64_t range_lo(const LastRound& r, int g, int n_wg) {
-  return r.units * g / n_wg;
+// Leftover range k in remainder units (rem * r of them).
+__host__ __device__ inline int64_t left_lo(const LastRound& lr, int k) {
+  return int64_t(lr.rem) * lr.r * k / lr.left;
 }
-// The workgroup whose range holds unit u (u < units).
-__host__ __device__ inline int range_of(const LastRound& r, int64_t u, int n_wg) {
-  int g = int(u * n_wg / r.units);
-  while (g + 1 < n_wg && range_lo(r, g + 1, n_wg) <= u) ++g;
-  while (g > 0 && range_lo(r, g, n_wg) > u) --g;
-  return g;
+// The leftover range that holds remainder unit u.
+__host__ __device__ inline int left_of(const LastRound& lr, int64_t u) {
+  int k = int(u * lr.left / (int64_t(lr.rem) * lr.r));
+  while (k + 1 < lr.left && left_lo(lr, k + 1) <= u) ++k;
+  while (k > 0 && left_lo(lr, k) > u) --k;
+  return k;
 }
 
 template <int D, int NW, bool W64>
@@ -808,23 +825,40 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch 
   for (int p = 0; p < a.n_pairs; ++p) {
     const PairLaunch& P = a.pair[p];
     const LastRound lr = last_round(P.n_items, P.ntiles, a.n_wg);
-    const int64_t lo = lr.rem ? range_lo(lr, g, a.n_wg) : 0, hi = lr.rem ? range_lo(lr, g + 1, a.n_wg) : 0;
-    // Pieces of this workgroup: lr.full whole items, then its last-round range
-    // (one call site, so the item body is inlined once).
+    // Pieces of this workgroup: lr.full whole items, then its last-round
+    // share (one call site, so the item body is inlined once).
+    const bool lev = lr.rem && g < lr.m * lr.rem;
+    const int k = g - lr.m * lr.rem;
+    int64_t pos = 0, hi = 0;
+    if (lr.rem && !lev && lr.r > 0) {
+      pos = left_lo(lr, k);
+      hi = left_lo(lr, k + 1);
+    }
+    bool lev_todo = lev;
     int u = 0;
-    for (int64_t pos = lo;;) {
+    for (;;) {
       int item, t_begin = 0, t_end = P.ntiles;
       float* slot = nullptr;
       if (u < lr.full) {
         item = u * a.n_wg + g;
         ++u;
-      } else if (pos < hi) {
-        const int x = int(pos / P.ntiles);
-        t_begin = int(pos - int64_t(x) * P.ntiles);
-        t_end = int(min(int64_t(P.ntiles), hi - int64_t(x) * P.ntiles));
-        slot = P.part + (int64_t(g) * 2 + (pos == lo ? 0 : 1)) * a.slot_floats;
+      } else if (lev_todo) {
+        lev_todo = false;
+        const int j = g / lr.rem, x = g % lr.rem;
+        t_begin = level_start(lr, j);
+        t_end = level_start(lr, j + 1);
+        if (t_begin >= t_end) break;
         item = lr.full * a.n_wg + x;
-        pos = int64_t(x) * P.ntiles + t_end;
+        slot = P.part + int64_t(g) * a.slot_floats;
+      } else if (pos < hi) {
+        const int x = int(pos / lr.r);
+        const int64_t off = pos - int64_t(x) * lr.r;
+        const int64_t end = min(int64_t(lr.r), hi - int64_t(x) * lr.r);
+        t_begin = lr.fm + int(off);
+        t_end = lr.fm + int(end);
+        item = lr.full * a.n_wg + x;
+        slot = P.part + (int64_t(lr.m) * lr.rem + x + k) * a.slot_floats;
+        pos = int64_t(x) * lr.r + end;
       } else {
         break;
       }
@@ -854,11 +888,24 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
   if (x >= lr.rem) return;
   const int item = lr.full * a.n_wg + x;
   const int qt = item % a.n_qtiles, h = item / a.n_qtiles;
-  // Pieces: the non-empty ranges of workgroups g0..g1; the piece of g0 is its
-  // second unless its range starts at this item.
-  const int64_t u0 = int64_t(x) * P.ntiles, u1 = u0 + P.ntiles - 1;
-  const int g0 = range_of(lr, u0, a.n_wg), g1 = range_of(lr, u1, a.n_wg);
-  const int first = range_lo(lr, g0, a.n_wg) < u0 ? 1 : 0;
+  // Pieces in key order: the non-empty levels j (slot j*rem + x), then the
+  // non-empty leftover ranges k0..k1 that hold the item's remainder (slot
+  // m*rem + x + k).
+  int k0 = 0, k1 = -1;
+  if (lr.r > 0) {
+    k0 = left_of(lr, int64_t(x) * lr.r);
+    k1 = left_of(lr, int64_t(x) * lr.r + lr.r - 1);
+  }
+  auto slot_of = [&](int n) -> const float* {   // n-th candidate piece, or null
+    if (n < lr.m) {
+      if (level_start(lr, n) >= level_start(lr, n + 1)) return nullptr;
+      return P.part + (int64_t(n) * lr.rem + x) * a.slot_floats;
+    }
+    const int kk = k0 + (n - lr.m);
+    if (left_lo(lr, kk) == left_lo(lr, kk + 1)) return nullptr;
+    return P.part + (int64_t(lr.m) * lr.rem + x + kk) * a.slot_floats;
+  };
+  const int n_cand = lr.m + (k1 - k0 + 1);
   const int c4 = threadIdx.x % TPR;
   const int r0 = (blockIdx.x % (BM / kMergeRows)) * kMergeRows + threadIdx.x / TPR;
   constexpr int NP = kMergeRows / RPP;           // rows per thread
@@ -873,13 +920,9 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
   // Two sweeps over the pieces (the row max, then the weighted sums); the
   // rows past lq read the slots' unwritten rows and are not stored.
   for (int sweep = 0; sweep < 2; ++sweep) {
-    int64_t lo_g = range_lo(lr, g0, a.n_wg);
-    for (int g = g0; g <= g1; ++g) {
-      const int64_t lo_n = range_lo(lr, g + 1, a.n_wg);
-      const bool empty = lo_g == lo_n;
-      lo_g = lo_n;
-      if (empty) continue;
-      const float* sp = P.part + (int64_t(g) * 2 + (g == g0 ? first : 0)) * a.slot_floats;
+    for (int n = 0; n < n_cand; ++n) {
+      const float* sp = slot_of(n);
+      if (!sp) continue;
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
         const int row = r0 + j * RPP;
