@@ -188,7 +188,7 @@ ff_status ff_render_attend_grouped(ff_ctx* ctx, int n_pairs, const int* chunks, 
  * graph capture, tight serving loops, harnesses that forbid allocation.
  * Same arguments, validation, results and bank update as ff_render_attend;
  * the only difference is where the call's split-item partials live: in a
- * fixed device array of the library (65 MiB, one per device, held until
+ * fixed device array of the library (130 MiB, one per device, held until
  * the process ends) instead of the workspace's partial region.  The call
  * itself allocates nothing.  Its first call on a device takes that array's
  * address (host metadata only).  Every call on one device shares the array
