@@ -890,22 +890,26 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
   const int qt = item % a.n_qtiles, h = item / a.n_qtiles;
   // Pieces in key order: the non-empty levels j (slot j*rem + x), then the
   // non-empty leftover ranges k0..k1 that hold the item's remainder (slot
-  // m*rem + x + k).
+  // m*rem + x + k).  The slot list is built once per block in LDS.
+  constexpr int kMaxCand = 2 * kMaxWg;
+  __shared__ int32_t cand[kMaxCand];
   int k0 = 0, k1 = -1;
   if (lr.r > 0) {
     k0 = left_of(lr, int64_t(x) * lr.r);
     k1 = left_of(lr, int64_t(x) * lr.r + lr.r - 1);
   }
-  auto slot_of = [&](int n) -> const float* {   // n-th candidate piece, or null
+  const int n_cand = lr.m + (k1 - k0 + 1);     // <= n_wg + left < kMaxCand
+  for (int n = threadIdx.x; n < n_cand; n += blockDim.x) {
+    int32_t slot = -1;
     if (n < lr.m) {
-      if (level_start(lr, n) >= level_start(lr, n + 1)) return nullptr;
-      return P.part + (int64_t(n) * lr.rem + x) * a.slot_floats;
+      if (level_start(lr, n) < level_start(lr, n + 1)) slot = n * lr.rem + x;
+    } else {
+      const int kk = k0 + (n - lr.m);
+      if (left_lo(lr, kk) < left_lo(lr, kk + 1)) slot = lr.m * lr.rem + x + kk;
     }
-    const int kk = k0 + (n - lr.m);
-    if (left_lo(lr, kk) == left_lo(lr, kk + 1)) return nullptr;
-    return P.part + (int64_t(lr.m) * lr.rem + x + kk) * a.slot_floats;
-  };
-  const int n_cand = lr.m + (k1 - k0 + 1);
+    cand[n] = slot;
+  }
+  __syncthreads();
   const int c4 = threadIdx.x % TPR;
   const int r0 = (blockIdx.x % (BM / kMergeRows)) * kMergeRows + threadIdx.x / TPR;
   constexpr int NP = kMergeRows / RPP;           // rows per thread
@@ -921,8 +925,9 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
   // rows past lq read the slots' unwritten rows and are not stored.
   for (int sweep = 0; sweep < 2; ++sweep) {
     for (int n = 0; n < n_cand; ++n) {
-      const float* sp = slot_of(n);
-      if (!sp) continue;
+      const int32_t slot = cand[n];
+      if (slot < 0) continue;
+      const float* sp = P.part + int64_t(slot) * a.slot_floats;
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
         const int row = r0 + j * RPP;
