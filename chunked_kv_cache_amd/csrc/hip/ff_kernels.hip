@@ -655,6 +655,28 @@ __device__ __forceinline__ void run_item_r64(const AttnLaunch& a, const PairLaun
   else if (t_begin + 1 < t_end) wait_dma_but<kDma>();
   else wait_dma();
   wg_barrier();
+  if (qt * BM + w * 64 >= lq) {
+    // No row of this wave exists (the last query tile of a head): it only
+    // keeps its part of the copies and the two barriers of every tile, and
+    // leaves its SIMD to the partner wave.
+    auto idle_tile = [&](int t, int i) {
+      wg_barrier();
+      if (t + 2 < t_end) wait_dma_but<kDma>();
+      else wait_dma();
+      wg_barrier();
+      if (t + 3 < t_end) issue(t + 3, (i + 3) & 3);
+    };
+    for (int t = t_begin; t < t_end; t += 4) {   // buffer indices known at compile time
+      idle_tile(t, 0);
+      if (t + 1 >= t_end) break;
+      idle_tile(t + 1, 1);
+      if (t + 2 >= t_end) break;
+      idle_tile(t + 2, 2);
+      if (t + 3 >= t_end) break;
+      idle_tile(t + 3, 3);
+    }
+    return;
+  }
   scores(lb.k[0], valid[0], 0, sa);
   // The first half of a piece holds at least one valid key, so m is finite.
 #pragma unroll
