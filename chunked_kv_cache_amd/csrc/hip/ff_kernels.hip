@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "../ff_internal.h"
+#include "../ff_schedule.h"
 #include "ff_prof.h"
 #include "ff_tile.h"
 
@@ -778,56 +779,6 @@ __device__ __forceinline__ void run_item_r64(const AttnLaunch& a, const PairLaun
   }
 }
 
-// Schedule of one call over n_wg persistent workgroups (one per CU).
-// Items run whole in full rounds (workgroup g takes item r*n_wg + g, so the
-// workgroups of an XCD stream one head's K/V in lockstep).  The rem items of
-// the last, partial round are cut along their key tiles into m = n_wg / rem
-// levels and a remainder: level j is the tile range [F(j), F(j+1)) of every
-// item, run by workgroups j*rem .. j*rem + rem-1 (again in lockstep, one item
-// each); the remainders [F(m), ntiles) of all items, item-major, are cut into
-// equal contiguous ranges for the n_wg - m*rem leftover workgroups, each of
-// which runs several short pieces.  F(j) = j*rem*(ntiles + c)/n_wg with c =
-// kPieceCost tiles, the cost of a piece's start and partial write, so that a
-// level piece and a leftover range (with its pieces) take about as long.
-// Every piece leaves a partial (O, m, l) in its own slot (level piece of
-// workgroup g: slot g; remainder piece of item x in leftover range k: slot
-// m*rem + x + k, below 2*n_wg) and the merge kernel combines an item's pieces
-// in key order.
-constexpr int kPieceCost = 6;
-struct LastRound {
-  int full, rem, m, left, ntiles, n_wg;
-  int fm;                          // F(m): first tile of the remainders
-  int r;                           // remainder tiles per item
-};
-__host__ __device__ inline int level_start(const LastRound& lr, int j) {
-  if (j >= lr.m && lr.left == 0) return lr.ntiles;
-  const int64_t f = int64_t(j) * lr.rem * (lr.ntiles + kPieceCost) / lr.n_wg;
-  return f < lr.ntiles ? int(f) : lr.ntiles;
-}
-__host__ __device__ inline LastRound last_round(int n_items, int ntiles, int n_wg) {
-  LastRound lr;
-  lr.full = n_items / n_wg;
-  lr.rem = n_items % n_wg;
-  lr.ntiles = ntiles;
-  lr.n_wg = n_wg;
-  lr.m = lr.rem ? n_wg / lr.rem : 0;
-  lr.left = n_wg - lr.m * lr.rem;
-  lr.fm = lr.rem ? level_start(lr, lr.m) : ntiles;
-  lr.r = ntiles - lr.fm;
-  return lr;
-}
-// Leftover range k in remainder units (rem * r of them).
-__host__ __device__ inline int64_t left_lo(const LastRound& lr, int k) {
-  return int64_t(lr.rem) * lr.r * k / lr.left;
-}
-// The leftover range that holds remainder unit u.
-__host__ __device__ inline int left_of(const LastRound& lr, int64_t u) {
-  int k = int(u * lr.left / (int64_t(lr.rem) * lr.r));
-  while (k + 1 < lr.left && left_lo(lr, k + 1) <= u) ++k;
-  while (k > 0 && left_lo(lr, k) > u) --k;
-  return k;
-}
-
 template <int D, int NW, bool W64>
 __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch a) {
   // One array per tile buffer, so that the compiler sees the copies into one
@@ -847,43 +798,12 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_bf16_kernel(const AttnLaunch 
   for (int p = 0; p < a.n_pairs; ++p) {
     const PairLaunch& P = a.pair[p];
     const LastRound lr = last_round(P.n_items, P.ntiles, a.n_wg);
-    // Pieces of this workgroup: lr.full whole items, then its last-round
-    // share (one call site, so the item body is inlined once).
-    const bool lev = lr.rem && g < lr.m * lr.rem;
-    const int k = g - lr.m * lr.rem;
-    int64_t pos = 0, hi = 0;
-    if (lr.rem && !lev && lr.r > 0) {
-      pos = left_lo(lr, k);
-      hi = left_lo(lr, k + 1);
-    }
-    bool lev_todo = lev;
-    int u = 0;
-    for (;;) {
-      int item, t_begin = 0, t_end = P.ntiles;
-      float* slot = nullptr;
-      if (u < lr.full) {
-        item = u * a.n_wg + g;
-        ++u;
-      } else if (lev_todo) {
-        lev_todo = false;
-        const int j = g / lr.rem, x = g % lr.rem;
-        t_begin = level_start(lr, j);
-        t_end = level_start(lr, j + 1);
-        if (t_begin >= t_end) break;
-        item = lr.full * a.n_wg + x;
-        slot = P.part + int64_t(g) * a.slot_floats;
-      } else if (pos < hi) {
-        const int x = int(pos / lr.r);
-        const int64_t off = pos - int64_t(x) * lr.r;
-        const int64_t end = min(int64_t(lr.r), hi - int64_t(x) * lr.r);
-        t_begin = lr.fm + int(off);
-        t_end = lr.fm + int(end);
-        item = lr.full * a.n_wg + x;
-        slot = P.part + (int64_t(lr.m) * lr.rem + x + k) * a.slot_floats;
-        pos = int64_t(x) * lr.r + end;
-      } else {
-        break;
-      }
+    // Pieces of this workgroup (one call site, so the item body is inlined
+    // once).
+    PieceIter it(lr, g);
+    int item, t_begin, t_end, si;
+    while (it.next(lr, item, t_begin, t_end, si)) {
+      float* slot = si < 0 ? nullptr : P.part + int64_t(si) * a.slot_floats;
       if constexpr (W64) run_item_r64<D>(a, P, item, t_begin, t_end, slot, lb);
       else run_item<D, NW>(a, P, item, t_begin, t_end, slot, lb);
     }
@@ -910,27 +830,12 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(const AttnLaunch a) {
   if (x >= lr.rem) return;
   const int item = lr.full * a.n_wg + x;
   const int qt = item % a.n_qtiles, h = item / a.n_qtiles;
-  // Pieces in key order: the non-empty levels j (slot j*rem + x), then the
-  // non-empty leftover ranges k0..k1 that hold the item's remainder (slot
-  // m*rem + x + k).  The slot list is built once per block in LDS.
+  // The item's pieces in key order, listed once per block in LDS.
   constexpr int kMaxCand = 2 * kMaxWg;
   __shared__ int32_t cand[kMaxCand];
-  int k0 = 0, k1 = -1;
-  if (lr.r > 0) {
-    k0 = left_of(lr, int64_t(x) * lr.r);
-    k1 = left_of(lr, int64_t(x) * lr.r + lr.r - 1);
-  }
-  const int n_cand = lr.m + (k1 - k0 + 1);     // <= n_wg + left < kMaxCand
-  for (int n = threadIdx.x; n < n_cand; n += blockDim.x) {
-    int32_t slot = -1;
-    if (n < lr.m) {
-      if (level_start(lr, n) < level_start(lr, n + 1)) slot = n * lr.rem + x;
-    } else {
-      const int kk = k0 + (n - lr.m);
-      if (left_lo(lr, kk) < left_lo(lr, kk + 1)) slot = lr.m * lr.rem + x + kk;
-    }
-    cand[n] = slot;
-  }
+  const MergeList ml(lr, x);
+  const int n_cand = ml.count(lr);             // <= n_wg + left < kMaxCand
+  for (int n = threadIdx.x; n < n_cand; n += blockDim.x) cand[n] = ml.slot(lr, n);
   __syncthreads();
   const int c4 = threadIdx.x % TPR;
   const int r0 = (blockIdx.x % (BM / kMergeRows)) * kMergeRows + threadIdx.x / TPR;

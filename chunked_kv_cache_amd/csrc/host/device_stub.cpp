@@ -5,6 +5,7 @@
 #include <cstring>
 
 #include "../ff_internal.h"
+#include "../ff_schedule.h"
 
 namespace ff {
 
@@ -120,5 +121,32 @@ int ffstub_last_copy_job(int j, const void** rows_k, const void** rows_v, int* n
 // Destination block of job j of the last copy launch, as a byte offset from ws.
 long long ffstub_last_copy_block(int j, const void* ws) {
   return static_cast<const char*>(ff::g_last_copy.job[j].block) - static_cast<const char*>(ws);
+}
+// Attention schedule of one call (the kernel's own enumeration): the pieces
+// of every workgroup as (g, item, t_begin, t_end, slot) rows; returns the
+// row count, or -1 past cap rows.
+int ffstub_schedule_pieces(int n_items, int ntiles, int n_wg, int* out, int cap) {
+  const ff::LastRound lr = ff::last_round(n_items, ntiles, n_wg);
+  int n = 0;
+  for (int g = 0; g < n_wg; ++g) {
+    ff::PieceIter it(lr, g);
+    int item, tb, te, slot;
+    while (it.next(lr, item, tb, te, slot)) {
+      if (n >= cap) return -1;
+      int* r = out + 5 * n++;
+      r[0] = g; r[1] = item; r[2] = tb; r[3] = te; r[4] = slot;
+    }
+  }
+  return n;
+}
+// The merge kernel's slot list of last-round item x (-1 for an empty
+// candidate); returns the candidate count, or -1 past cap.
+int ffstub_merge_slots(int n_items, int ntiles, int n_wg, int x, int* out, int cap) {
+  const ff::LastRound lr = ff::last_round(n_items, ntiles, n_wg);
+  const ff::MergeList ml(lr, x);
+  const int n = ml.count(lr);
+  if (n > cap) return -1;
+  for (int i = 0; i < n; ++i) out[i] = ml.slot(lr, i);
+  return n;
 }
 }
