@@ -225,6 +225,17 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bc_dq_kernel(const BcLaunch 
 
   set_source(0);
   int valid = issue(0);
+  if (qt * kBlockM + w * 32 >= b.L) {
+    // No query row of this wave exists (the last tile of a chunk): it keeps
+    // its part of the copies and the barriers and leaves its SIMD to the
+    // other wave.
+    for (int t = 0; t < ntiles; ++t) {
+      wait_dma();
+      __syncthreads();
+      if (t + 1 < ntiles) issue((t & 1) ^ 1);
+    }
+    return;
+  }
   for (int t = 0; t < ntiles; ++t) {
     const int p = t & 1;
     wait_dma();
@@ -345,6 +356,17 @@ __global__ __launch_bounds__(kKeyWaves * 64, 1) void bc_dkv_kernel(const BcLaunc
   };
 
   int valid = ntiles > 0 ? issue(0, 0) : 0;
+  if (kb * kKeyBlock + w * 32 >= n) {
+    // No key of this wave exists (the last block of a source): it keeps its
+    // part of the copies and the barriers and leaves its SIMD to the other
+    // wave.  (Wave 0, which also copies the row statistics, always has keys.)
+    for (int t = 0; t < ntiles; ++t) {
+      wait_dma();
+      __syncthreads();
+      if (t + 1 < ntiles) issue(t + 1, (t & 1) ^ 1);
+    }
+    return;
+  }
   for (int t = 0; t < ntiles; ++t) {
     const int p = t & 1;
     wait_dma();
