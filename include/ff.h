@@ -118,7 +118,7 @@ typedef struct {
 /* Accumulated device time per kernel family while profiling is enabled. */
 typedef struct {
   int64_t attn_launches;    double attn_ms;      /* segmented attention        */
-  int64_t merge_launches;   double merge_ms;     /* split-K LSE merge          */
+  int64_t merge_launches;   double merge_ms;     /* merge of split items        */
   int64_t publish_launches; double publish_ms;   /* Tail_H stage-bank publish  */
   int64_t anchor_launches;  double anchor_ms;    /* anchor-bank publish        */
   int64_t layout_launches;  double layout_ms;    /* block-causal operand copies */
