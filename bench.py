@@ -223,6 +223,11 @@ def main():
         f"publish {pub_ms * 1e3:.1f} us ({pub_gbps:.0f} GB/s), step {ms_per_step:.3f} ms "
         f"(median {steps_ms['median']:.3f}, min {steps_ms['min']:.3f}); clocks {clock_info}")
 
+    copy_us, copy_med_us = publish_copy_reference(one_step, steps_done + args.steps, pub_bytes)
+    copy_gbps = pub_bytes / (copy_us * 1e-6) / 1e9
+    log(f"device copy of the publish's bytes after a step: {copy_us:.1f} us ({copy_gbps:.0f} GB/s); "
+        f"publish / copy rate {pub_gbps / copy_gbps:.2f}")
+
     if args.calibration_copy:
         calibration_copy()
 
@@ -255,6 +260,12 @@ def main():
         "publish_kernel_us": round(pub_ms * 1e3, 2),
         "publish_gbps": round(pub_gbps, 1),
         "publish_pct_hbm": round(100 * pub_gbps / PEAK_HBM_GBPS, 2),
+        "publish_copy_reference": {
+            "what": "one hipMemcpyAsync (torch copy_) of the same bytes (a chunk's K and V, read once and written "
+                    "once), event-timed right after a step, 8 rotating sources",
+            "us": round(copy_us, 2), "median_us": round(copy_med_us, 2), "gbps": round(copy_gbps, 1),
+            "pct_hbm": round(100 * copy_gbps / PEAK_HBM_GBPS, 2),
+            "publish_over_copy": round(pub_gbps / copy_gbps, 3)},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload)},
@@ -322,6 +333,29 @@ def step_stats(events):
     ms = sorted(a.elapsed_time(b) for a, b in events)
     return {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4), "mean": round(sum(ms) / len(ms), 4),
             "n": len(ms)}
+
+
+def publish_copy_reference(one_step, j0, n_bytes, n=40):
+    """The platform's device copy of the publish's bytes, for comparison: after
+    each of n further steps, one hipMemcpyAsync (torch copy_) of n_bytes/2
+    bytes (a chunk's K and V: n_bytes counts each byte read and written)
+    between buffers that rotate over 8 sources and 4 destinations, bracketed
+    by its own events -- the conditions of the publish, which also follows a
+    step's kernels.  Returns the mean and median time in us."""
+    import torch
+    half = n_bytes // 2
+    srcs = [torch.randint(0, 255, (half,), dtype=torch.uint8, device="cuda") for _ in range(8)]
+    dsts = [torch.empty(half, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for j in range(n):
+        one_step(j0 + j)
+        ev[j][0].record()
+        dsts[j % 4].copy_(srcs[j % 8])
+        ev[j][1].record()
+    torch.cuda.synchronize()
+    us = sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+    return sum(us) / n, us[n // 2]
 
 
 def calibration_copy():

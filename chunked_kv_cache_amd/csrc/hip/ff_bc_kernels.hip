@@ -80,6 +80,65 @@ __device__ __forceinline__ void tr_mfma_half(const uint8_t* tbuf, int half, cons
     }
 }
 
+// One 32-row half of a backward tile as a single stream of LDS operand
+// reads, each issued kBwdAhead MFMAs before its use (every read feeds one
+// MFMA, which alone does not cover the read's latency):
+//   the score MFMAs  sc += A x areg (A = rows tile abuf) and, with kDP,
+//                    dp += G x greg (G = rows tile gbuf), alternating so that
+//                    the two accumulator chains interleave;
+//   pre()            at the last score MFMA (loads the valu step's inputs);
+//   valu(sc, dp, ob) the weights of the half as two bf16 B operands;
+//   the accumulation acc[db] += T[32*db ..][half] x ob (T = transposed tile
+//                    tbuf), whose first reads are in flight under the valu.
+constexpr int kBwdAhead = 3;
+
+template <int D, int NW, bool kDP, typename Pre, typename Valu>
+__device__ __forceinline__ void bwd_half(const uint8_t* abuf, const uint8_t* gbuf, const uint8_t* tbuf, int half,
+                                         const LaneConst<D, NW>& lc, const bf16x8 (&areg)[1][D / 16],
+                                         const bf16x8 (&greg)[1][D / 16], f32x16 (&acc)[D / 32], Pre&& pre,
+                                         Valu&& valu) {
+  constexpr int KS = D / 16, DB = D / 32;
+  constexpr int NSC = kDP ? 2 * KS : KS;       // score MFMAs
+  constexpr int N = NSC + 2 * DB;              // + accumulation MFMAs
+  auto rd = [&](int k) {
+    if (k < NSC) {
+      const int ks = kDP ? k >> 1 : k;
+      const uint8_t* buf = (kDP && (k & 1)) ? gbuf : abuf;
+      return __builtin_bit_cast(bf16x8, ld16(buf + lc.kread[ks] + half * 32 * D * 2));
+    }
+    const int m = k - NSC, j = m / DB, db = m % DB;
+    return __builtin_bit_cast(
+        bf16x8, ld16(tbuf + (int32_t(lc.vread[half][j]) - int32_t(kLdsBias)) + db * 32 * kBlockN * 2));
+  };
+  f32x16 sc = {}, dp = {};
+  bf16x8 ob[2];
+  bf16x8 op[kBwdAhead + 1];
+#pragma unroll
+  for (int j = 0; j < kBwdAhead; ++j) op[j] = rd(j);
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    op[kBwdAhead] = op[kBwdAhead - 1];
+    if (k + kBwdAhead < N) op[kBwdAhead] = rd(k + kBwdAhead);
+    if (k == NSC - 1) pre();
+    __builtin_amdgcn_sched_barrier(0);
+    if (k == NSC) {
+      valu(sc, dp, ob);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (k < NSC) {
+      const int ks = kDP ? k >> 1 : k;
+      if (kDP && (k & 1)) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[0], greg[0][ks], dp, 0, 0, 0);
+      else sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[0], areg[0][ks], sc, 0, 0, 0);
+    } else {
+      const int m = k - NSC, j = m / DB, db = m % DB;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op[0], ob[j], acc[db], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kBwdAhead; ++j) op[j] = op[j + 1];
+  }
+}
+
 // Row r of a bf16 token-major tensor, head h, as this lane's B operand over
 // head_dim: 8 values per 16-wide k-step (zeros when !ok).
 template <int D>
@@ -246,20 +305,19 @@ __global__ __launch_bounds__(kDqWaves * 64, 1) void bc_dq_kernel(const BcLaunch 
     const uint8_t* tb = p ? kt1 : kt0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      f32x16 sc[1], dp[1];
-      qk_half<D, NW, 1>(kb, half, lc, qreg, sc);
-      qk_half<D, NW, 1>(vb, half, lc, greg, dp);
       const int lim = valid - 32 * half;
-      if (lim < 32) mask_half(sc[0], lim, hl);
-      bf16x8 dsb[2];
+      bwd_half<D, NW, true>(
+          kb, vb, tb, half, lc, qreg, greg, acc, [] {},
+          [&](f32x16& sc, const f32x16& dp, bf16x8 (&dsb)[2]) {
+            if (lim < 32) mask_half(sc, lim, hl);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[0][8 * j + e], c, nl));
-          dsb[j][e] = (__bf16)(pv * (dp[0][8 * j + e] - dl));
-        }
-      tr_mfma_half<D, NW>(tb, half, lc, dsb, acc);
+              for (int e = 0; e < 8; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sc[8 * j + e], c, nl));
+                dsb[j][e] = (__bf16)(pv * (dp[8 * j + e] - dl));
+              }
+          });
     }
     valid = valid_next;
   }
@@ -378,29 +436,31 @@ __global__ __launch_bounds__(kKeyWaves * 64, 1) void bc_dkv_kernel(const BcLaunc
     const float* stb = reinterpret_cast<const float*>(p ? st1 : st0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      f32x16 sc[1], dp[1];
-      qk_half<D, NW, 1>(qb, half, lc, kreg, sc);
-      if (kDK) qk_half<D, NW, 1>(gb, half, lc, vreg, dp);
       const int lim = valid - 32 * half;
-      if (lim < 32) mask_half(sc[0], lim, hl);
-      bf16x8 ob[2];
+      // The statistics of the half's queries: registers 8j .. 8j+7 hold
+      // queries 32*half + 16j + 8*hl + 0..7.
+      float4 stv[2][4];
+      bwd_half<D, NW, kDK>(
+          qb, gb, tb, half, lc, kreg, vreg, acc,
+          [&] {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        // registers 8j .. 8j+7 hold queries 32*half + 16j + 8*hl + 0..7
-        const float* sq = stb + 2 * (32 * half + 16 * j + 8 * hl);
-        float stv[16];
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float4 v = reinterpret_cast<const float4*>(sq)[u];
-          stv[4 * u] = v.x; stv[4 * u + 1] = v.y; stv[4 * u + 2] = v.z; stv[4 * u + 3] = v.w;
-        }
+              for (int u = 0; u < 4; ++u)
+                stv[j][u] = reinterpret_cast<const float4*>(stb + 2 * (32 * half + 16 * j + 8 * hl))[u];
+          },
+          [&](f32x16& sc, const f32x16& dp, bf16x8 (&ob)[2]) {
+            if (lim < 32) mask_half(sc, lim, hl);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sc[0][8 * j + e], c, stv[2 * e]));
-          ob[j][e] = kDK ? (__bf16)(pv * (dp[0][8 * j + e] - stv[2 * e + 1])) : (__bf16)pv;
-        }
-      }
-      tr_mfma_half<D, NW>(tb, half, lc, ob, acc);
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float4 v = stv[j][e >> 1];
+                const float nl = (e & 1) ? v.z : v.x, dl = (e & 1) ? v.w : v.y;
+                const float pv = __builtin_amdgcn_exp2f(fmaf(sc[8 * j + e], c, nl));
+                ob[j][e] = kDK ? (__bf16)(pv * (dp[8 * j + e] - dl)) : (__bf16)pv;
+              }
+          });
     }
     valid = valid_next;
   }
