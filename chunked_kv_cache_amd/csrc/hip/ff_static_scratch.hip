@@ -14,7 +14,7 @@
 
 namespace ff {
 
-__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
 
 int dev_static_scratch(void** ptr, size_t* bytes) {
   static std::mutex mu;
