@@ -220,8 +220,11 @@ class Pair:
         return results
 
     def plan_step(self, b: int, step: int, publish: bool, rows: Optional[np.ndarray] = None,
-                  control: bool = False):
-        """One planner call of block b at denoising step `step` on the GPU, then the oracle."""
+                  control: bool = False, whole_heads=()):
+        """One planner call of block b at denoising step `step` on the GPU, then the oracle.
+        `whole_heads`: heads whose every query row is also compared (one head's
+        keys at a time); returns (head, max |dO|, relative Frobenius) per such head
+        as a third value."""
         import torch
         c = self.case
         blk = orc.planner_blocks(self.cfg)[b]
@@ -242,6 +245,21 @@ class Pair:
         if control:
             qc = q64 if rows is None else q64[rows]
             ctrl, _ = orc.attention(qc, k64, v64, self.cfg.scale)        # own latents only
+        whole = []
+        if whole_heads:
+            O_all = from_device_f64(out)
+            L_all = lse.cpu().numpy().astype(np.float64)
+            for hh in whole_heads:
+                h1 = lambda x: np.asarray(x)[:, hh:hh + 1]
+                ks = [h1(self.ro.anchors[a][0]) for kind, a in srcs if kind == "anchor"] + [h1(k64)]
+                vs = [h1(self.ro.anchors[a][1]) for kind, a in srcs if kind == "anchor"] + [h1(v64)]
+                Oh, Lh = orc.attention(h1(q64), np.concatenate(ks), np.concatenate(vs), self.cfg.scale)
+                Og = O_all[:, hh:hh + 1]
+                err = float(np.abs(Og - Oh).max())
+                relf = float(np.linalg.norm(Og - Oh) / np.linalg.norm(Oh))
+                dl = float(np.abs(L_all[hh:hh + 1] - Lh).max())
+                assert err <= TOL[c.dtype] and relf <= RELF_TOL[c.dtype] and dl <= LSE_TOL[c.dtype], (hh, err, relf, dl)
+                whole.append((hh, err, relf))
         O_ref, L_ref = self.ro.plan_attend(b, q64, k64, v64, publish=publish, rows=rows)
         O = from_device_f64(out)
         L = lse.cpu().numpy().astype(np.float64)
@@ -254,6 +272,8 @@ class Pair:
         if publish:
             for j, a in enumerate(blk):
                 self.vmax[("anchor", a)] = float(np.abs(v64[j * c.T:(j + 1) * c.T]).max())
+        if whole_heads:
+            return O, O_ref, whole
         return O, O_ref
 
     def _control(self, i, k, host, rows):

@@ -176,7 +176,9 @@ def test_planner_rollout_bf16_multi_tile(h_p):
 def test_planner_480p_block_sampled_rows():
     """480p shape, 261 latents: blocks 0..8 published through their
     cache-extraction calls; block 8's denoising call reads 6 earlier blocks
-    (21 key latents, 4680 queries x 32760 keys), 32 sampled rows per call."""
+    (21 key latents, 4680 queries x 32760 keys), 32 sampled rows per call;
+    that call (the one the planner benchmark times) also whole on heads 0 and
+    11: every query row against the oracle over the head's 32760 keys."""
     import sys
     case = Case(T=1560, nh=12, d=128, n_latents=261, S=1)
     rows = np.sort(np.random.default_rng(3).choice(3 * 1560, size=32, replace=False))
@@ -184,7 +186,10 @@ def test_planner_480p_block_sampled_rows():
     try:
         for b in range(9):
             if b == 8:
-                pr.plan_step(b, 0, publish=False, rows=rows, control=True)
+                _, _, whole = pr.plan_step(b, 0, publish=False, rows=rows, control=True, whole_heads=(0, 11))
+                for hh, err, relf in whole:
+                    print(f"  planner block 8 head {hh}, all rows: max|dO|={err:.2e} relF={relf:.2e}", flush=True,
+                          file=sys.stderr)
             pr.plan_step(b, 1, publish=True, rows=rows)
             print(f"  planner block {b} ok", flush=True, file=sys.stderr)
         print(f"planner 480p: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
