@@ -249,8 +249,9 @@ def test_720p_step_sampled_rows():
     is the 20-latent step (10800 queries x 72000 keys) and chunk 13 the
     21-latent one (75600 keys, three anchors), the largest call of the
     workloads; 8 sampled query rows per call against the oracle, banks exact.
-    Chunk 13 is also checked whole on heads 0 and 39: all 10800 query rows
-    against the oracle over that head's 75600 keys."""
+    Chunks 5 (the call the 720p step benchmark times) and 13 are also checked
+    whole on heads 0 and 39: all 10800 query rows against the oracle over
+    that head's 72000 or 75600 keys."""
     import sys
 
     from ffharness import check_whole_heads, whole_head_reference
@@ -260,10 +261,10 @@ def test_720p_step_sampled_rows():
     try:
         pr.publish_anchors()
         for i in range(14):
-            whole = whole_head_reference(pr, 13, 0, (0, 39)) if i == 13 else {}
+            whole = whole_head_reference(pr, i, 0, (0, 39)) if i in (5, 13) else {}
             pr.step([(i, 0)], grouped=False, rows=rows, control=i in (5, 13))
             for hh, err, relf in check_whole_heads(pr, whole):
-                print(f"  720p chunk 13 head {hh}, all rows: max|dO|={err:.2e} relF={relf:.2e}", flush=True,
+                print(f"  720p chunk {i} head {hh}, all rows: max|dO|={err:.2e} relF={relf:.2e}", flush=True,
                       file=sys.stderr)
             print(f"  720p chunk {i} ok", flush=True, file=sys.stderr)
         print(f"720p chunks 0..13: max|dO|={pr.stats.max_abs:.2e} relF={pr.stats.max_rel_fro:.2e} "
