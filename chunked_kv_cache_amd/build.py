@@ -2,9 +2,10 @@
 
   libff.so            C ABI + gfx950 HIP kernels (hipcc, --offload-arch=gfx950):
                       ff_kernels.hip (renderer / planner attention, bank
-                      copies), ff_bc_kernels.hip (block-causal backward) and
+                      copies), ff_bc_kernels.hip (block-causal backward),
                       ff_static_scratch.hip (the fixed device scratch of the
-                      call that allocates nothing)
+                      call that allocates nothing) and ff_prof.hip (settings
+                      of the per-launch timing)
   libff_hostcheck.so  the same host bookkeeping linked against a recording stub
                       instead of the kernels (g++); CPU tests use it to drive the
                       ABI's success paths without a GPU.
@@ -47,7 +48,7 @@ def build(verbose_resources: bool = False) -> None:
 
     extra = ["-Rpass-analysis=kernel-resource-usage"] if verbose_resources else []
     kern_objs = []
-    for name in ("ff_kernels", "ff_bc_kernels", "ff_static_scratch"):
+    for name in ("ff_kernels", "ff_bc_kernels", "ff_static_scratch", "ff_prof"):
         src = os.path.join(CSRC, "hip", name + ".hip")
         obj = os.path.join(BUILD, name + ".o")
         _run([HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", *DEVICE_FLAGS, *extra, *inc,

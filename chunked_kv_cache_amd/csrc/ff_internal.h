@@ -163,6 +163,7 @@ int dev_launch_bc_backward(const BcLaunch& b, void* stream, Profiler* prof);
 Profiler* dev_profiler_create();
 void dev_profiler_destroy(Profiler* p);
 void dev_profiler_reset(Profiler* p);
+void dev_profiler_families(Profiler* p, unsigned families);   // bit f = kernel family f of ff_kernel_times
 int dev_profiler_read(Profiler* p, ff_kernel_times* out);
 
 inline int64_t elem_size(int dtype) { return dtype == FF_F32 ? 4 : 2; }

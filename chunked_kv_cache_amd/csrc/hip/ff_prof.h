@@ -20,6 +20,7 @@ struct Profiler {
   std::vector<hipEvent_t> pool;
   int64_t count[kKinds] = {};
   double ms[kKinds] = {};
+  unsigned families = ~0u;         // kinds that get event pairs
   hipEvent_t get() {
     if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
     hipEvent_t e = nullptr;
@@ -33,7 +34,7 @@ namespace {
 struct Timed {
   Profiler* p; int kind; hipStream_t s; hipEvent_t a = nullptr, b = nullptr;
   Timed(Profiler* p_, int k, hipStream_t s_) : p(p_), kind(k), s(s_) {
-    if (p) { a = p->get(); b = p->get(); if (a) (void)hipEventRecord(a, s); }
+    if (p && ((p->families >> k) & 1u)) { a = p->get(); b = p->get(); if (a) (void)hipEventRecord(a, s); }
   }
   ~Timed() {
     if (p && a && b) { (void)hipEventRecord(b, s); p->pending.push_back({kind, a, b}); }

@@ -59,6 +59,7 @@ int dev_static_scratch(void** ptr, size_t* bytes) {
 Profiler* dev_profiler_create() { return new Profiler(); }
 void dev_profiler_destroy(Profiler* p) { delete p; }
 void dev_profiler_reset(Profiler*) {}
+void dev_profiler_families(Profiler*, unsigned) {}
 int dev_profiler_read(Profiler*, ff_kernel_times* out) {
   std::memset(out, 0, sizeof(*out));
   return 0;

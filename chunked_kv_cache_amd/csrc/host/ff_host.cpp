@@ -33,6 +33,7 @@ struct ff_ctx {
   std::vector<uint8_t> can_rewind;
   Profiler* prof = nullptr;
   bool profiling = false;
+  unsigned prof_families = FF_PROF_ALL;
 };
 
 namespace {
@@ -603,8 +604,18 @@ ff_status ff_profile_enable(ff_ctx* c, int on) {
     c->prof = dev_profiler_create();
     if (!c->prof) return FF_E_HIP;
   }
-  if (c->prof) dev_profiler_reset(c->prof);
+  if (c->prof) {
+    dev_profiler_reset(c->prof);
+    dev_profiler_families(c->prof, c->prof_families);
+  }
   c->profiling = on != 0;
+  return FF_OK;
+}
+
+ff_status ff_profile_families(ff_ctx* c, unsigned families) {
+  if (!c || (families & ~unsigned(FF_PROF_ALL))) return FF_E_INVAL;
+  c->prof_families = families;
+  if (c->prof) dev_profiler_families(c->prof, families);
   return FF_OK;
 }
 

@@ -86,6 +86,7 @@ _SIGS = {
                           ctypes.POINTER(_I)]),
     "ff_profile_enable": (_I, [_VP, _I]),
     "ff_profile_read": (_I, [_VP, ctypes.POINTER(ff_kernel_times)]),
+    "ff_profile_families": (_I, [_VP, ctypes.c_uint]),
     "ff_bc_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(ff_shape), _I]),
     "ff_bc_create": (_I, [ctypes.POINTER(ff_shape), _I, _VP, ctypes.c_size_t, ctypes.POINTER(_VP)]),
     "ff_bc_destroy": (None, [_VP]),
@@ -269,6 +270,17 @@ def ff_wavefront(shape: ff_shape, n_stages: int, t: int, L=None):
 def ff_profile_enable(ctx, on: bool, L=None) -> None:
     L = L or lib()
     _check(L.ff_profile_enable(ctx, 1 if on else 0), L)
+
+
+# Kernel families of ff_kernel_times (bits of ff_profile_families).
+PROF_ATTN, PROF_MERGE, PROF_PUBLISH, PROF_ANCHOR, PROF_LAYOUT = 1, 2, 4, 8, 16
+PROF_BWD_PRE, PROF_BWD_DQ, PROF_BWD_DK, PROF_BWD_DV = 32, 64, 128, 256
+PROF_ALL = 511
+
+
+def ff_profile_families(ctx, families: int, L=None) -> None:
+    L = L or lib()
+    _check(L.ff_profile_families(ctx, families), L)
 
 
 def ff_profile_read(ctx, L=None) -> dict:

@@ -293,6 +293,17 @@ ff_status ff_plan_key_plan(const ff_ctx* ctx, int block, ff_key_sources* out);
  * the accumulated totals since enabling (enable also resets them).            */
 ff_status ff_profile_enable(ff_ctx* ctx, int on);
 ff_status ff_profile_read(ff_ctx* ctx, ff_kernel_times* out);
+/* ff_profile_families -- restrict the event pairs to the kernel families set
+ * in `families` (bit f = the f-th family of ff_kernel_times: FF_PROF_ATTN,
+ * FF_PROF_MERGE, ...; default FF_PROF_ALL).  Each event pair costs a few
+ * microseconds of stream time, so a caller timing a whole step can bracket
+ * only the kernel it needs.  Holds until changed, across enable/disable.     */
+enum {
+  FF_PROF_ATTN = 1 << 0, FF_PROF_MERGE = 1 << 1, FF_PROF_PUBLISH = 1 << 2, FF_PROF_ANCHOR = 1 << 3,
+  FF_PROF_LAYOUT = 1 << 4, FF_PROF_BWD_PRE = 1 << 5, FF_PROF_BWD_DQ = 1 << 6, FF_PROF_BWD_DK = 1 << 7,
+  FF_PROF_BWD_DV = 1 << 8, FF_PROF_ALL = (1 << 9) - 1
+};
+ff_status ff_profile_families(ff_ctx* ctx, unsigned families);
 
 /* ---------------------------------------------------------------------------
  * Block-causal renderer attention over a whole clip at one stage: the

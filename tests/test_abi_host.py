@@ -61,6 +61,28 @@ def test_product_library_rejects_before_device_work():
         ff.ff_destroy(ctx, L=L)
 
 
+def test_profile_families_are_validated():
+    """ff_profile_families takes only the bits of the ff_kernel_times families
+    (checked on the host, no device work) and holds across enable/disable."""
+    L = ff.load(ff.HOSTCHECK_PATH)
+    shape = ff.make_shape(n_heads=2, head_dim=128, tokens_per_latent=16)
+    need = ff.ff_workspace_bytes(shape, 1, 5, L=L)
+    buf, addr = _aligned_buffer(need)
+    ctx = ff.ff_stage_bank_create(shape, 1, 5, addr, need, L=L)
+    try:
+        for fam in (0, ff.PROF_ATTN, ff.PROF_PUBLISH | ff.PROF_MERGE, ff.PROF_ALL):
+            ff.ff_profile_families(ctx, fam, L=L)
+        with pytest.raises(ff.FFError) as e:
+            ff.ff_profile_families(ctx, ff.PROF_ALL + 1, L=L)
+        assert e.value.status == ff.FF_E_INVAL
+        ff.ff_profile_families(ctx, ff.PROF_ATTN, L=L)
+        ff.ff_profile_enable(ctx, True, L=L)
+        ff.ff_profile_enable(ctx, False, L=L)
+        assert ff.ff_profile_read(ctx, L=L)["attn_launches"] == 0
+    finally:
+        ff.ff_destroy(ctx, L=L)
+
+
 # --------------------------------------------------------------------------
 # Host-check library (recording stub instead of kernels)
 # --------------------------------------------------------------------------
