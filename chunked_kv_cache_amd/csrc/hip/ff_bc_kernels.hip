@@ -65,21 +65,6 @@ __device__ __forceinline__ void copy_tr(const __bf16* tr, int n, int o, const ui
   for (int j = 0; j < Cfg::kVBlocks; ++j) dma16(r, off[j], buf + (w * Cfg::kVBlocks + j) * 1024);
 }
 
-// acc[db] += T[32*db .. 32*db+31][rows of the half] x B, with T a transposed
-// tile in LDS and B the bf16 B operand over the half's 32 rows.
-template <int D, int NW>
-__device__ __forceinline__ void tr_mfma_half(const uint8_t* tbuf, int half, const LaneConst<D, NW>& lc,
-                                             const bf16x8 (&b)[2], f32x16 (&acc)[D / 32]) {
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const bf16x8 av = __builtin_bit_cast(
-          bf16x8, ld16(tbuf + (int32_t(lc.vread[half][j]) - int32_t(kLdsBias)) + db * 32 * kBlockN * 2));
-      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b[j], acc[db], 0, 0, 0);
-    }
-}
-
 // One 32-row half of a backward tile as a single stream of LDS operand
 // reads, each issued kBwdAhead MFMAs before its use (every read feeds one
 // MFMA, which alone does not cover the read's latency):
