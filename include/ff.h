@@ -297,7 +297,8 @@ ff_status ff_profile_read(ff_ctx* ctx, ff_kernel_times* out);
  * in `families` (bit f = the f-th family of ff_kernel_times: FF_PROF_ATTN,
  * FF_PROF_MERGE, ...; default FF_PROF_ALL).  Each event pair costs a few
  * microseconds of stream time, so a caller timing a whole step can bracket
- * only the kernel it needs.  Holds until changed, across enable/disable.     */
+ * only the kernel it needs.  Holds until changed, across enable/disable.
+ * Host only; FF_E_INVAL for a null ctx or bits outside FF_PROF_ALL.          */
 enum {
   FF_PROF_ATTN = 1 << 0, FF_PROF_MERGE = 1 << 1, FF_PROF_PUBLISH = 1 << 2, FF_PROF_ANCHOR = 1 << 3,
   FF_PROF_LAYOUT = 1 << 4, FF_PROF_BWD_PRE = 1 << 5, FF_PROF_BWD_DQ = 1 << 6, FF_PROF_BWD_DK = 1 << 7,
